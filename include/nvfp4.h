@@ -1,0 +1,209 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 library, libnvfp4.so.
+ *
+ * The format ("LongLive-2.0: An NVFP4 Parallel Infrastructure for Long Video
+ * Generation", architecture walkthrough page, section "NVFP4 Training",
+ * paragraphs "NVFP4 numeric format", "Hierarchical scaling" and
+ * "Quantization rule for a tensor block"):
+ *
+ *     Xhat = X_FP4 * alpha_FP8 * alpha_FP32
+ *
+ * X_FP4 is a 4-bit E2M1 code per element (values 0, +-0.5, +-1, +-1.5, +-2,
+ * +-3, +-4, +-6), alpha_FP8 an E4M3 scale shared by a block of 16 elements
+ * (or a 16x16 tile for weights, "NVFP4 training recipe"), alpha_FP32 one
+ * float per tensor.  The block scale maps the block max to 6, or -- rule
+ * NVFP4_RULE_4OVER6, the pages' "Four Over Six" scale search of section
+ * "NVFP4 Inference" -- to 4 when that reconstructs the block with a smaller
+ * squared error.
+ *
+ * Exact arithmetic of every step (fp32 evaluation order, rounding, ties,
+ * saturation) is fixed by this library as follows; the pages state the rule
+ * in real numbers only:
+ *   alpha   = amax / 2688 in fp32 (2688 = 448 * 6); alpha = 1 if amax == 0
+ *   mu      = m / alpha, m the block's max |x|
+ *   s_c     = E4M3(mu / c), c in {6, 4}: nearest, ties to even, subnormals
+ *             kept, saturating at 448
+ *   code    = E2M1(x * (1 / (s_c * alpha))): nearest, ties to even,
+ *             saturating at 6, sign of x kept (-0.0 -> code 0x8); s_c == 0
+ *             gives +-0 codes
+ *   xhat    = (q * s) * alpha                    (two fp32 multiplies)
+ *   error_c = per block row, fma chain e = fma(d, d, e) over the row's 16
+ *             elements in index order, d = x - xhat; rows added in order;
+ *             4 is chosen only if error_4 < error_6.
+ *
+ * Layouts (row-major, element 2j in the LOW nibble of byte j, scales are
+ * E4M3FN bytes):
+ *   NVFP4_ROW16  x [rows][cols], blocks of 16 along cols (activations,
+ *                gradients, KV).  codes [rows][cols/2], scales [rows][cols/16].
+ *   NVFP4_TILE16 x [rows][cols], 16x16 tiles (weights).
+ *                codes [rows][cols/2], scales [rows/16][cols/16].
+ *   NVFP4_COL16  x [rows][cols], blocks of 16 along ROWS (the contraction
+ *                dimension of the weight-gradient GEMM); stored transposed so
+ *                that dimension is contiguous: codes [cols][rows/2], scales
+ *                [cols][rows/16].  This is exactly the ROW16 packing of x^T.
+ *   alpha        one float (device memory).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates or frees device memory and keeps no state
+ *     between calls.  Work is enqueued on `stream` (0 = null stream) and is
+ *     asynchronous; buffers must stay alive until the stream reaches it.
+ *   - Inputs must not alias outputs or the workspace.
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing is enqueued and outputs are untouched.  Launch failures are
+ *     reported as NVFP4_ERR_LAUNCH.  No C++ exception crosses the ABI.
+ *   - Alignment: codes, scales and workspaces 16-byte aligned.  Inputs read
+ *     and outputs written in 16-byte vectors (ROW16/TILE16 quantize input,
+ *     ROW16/TILE16 dequantize output, nvfp4_linear's x) need a 16-byte
+ *     aligned pointer and a leading dimension that is a multiple of 8
+ *     elements; every other tensor (COL16 input, GEMM output, ...) only
+ *     needs element alignment.  Leading dimensions are >= the row length.
+ *   - Numeric contract: inputs finite and amax == 0 or amax >= 2^-96;
+ *     otherwise results are unspecified, but no call faults.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,       /* a size is negative, too large or not a multiple of 16 where required */
+    NVFP4_ERR_ALIGN = 3,       /* pointer or leading dimension misaligned */
+    NVFP4_ERR_DTYPE = 4,       /* unknown dtype / block / rule enum value */
+    NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    NVFP4_ERR_LAUNCH = 6       /* a kernel launch failed (hipGetLastError) */
+} nvfp4_status_t;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
+typedef enum { NVFP4_RULE_STATIC6 = 0, NVFP4_RULE_4OVER6 = 1 } nvfp4_rule_t;
+typedef enum { NVFP4_ROW16 = 0, NVFP4_TILE16 = 1, NVFP4_COL16 = 2 } nvfp4_block_t;
+
+/* Scale layout of a packed GEMM operand (see nvfp4_gemm). */
+typedef enum { NVFP4_SCALE_1D = 0, NVFP4_SCALE_2D = 1 } nvfp4_scale_layout_t;
+
+int nvfp4_abi_version(void);
+const char *nvfp4_status_string(nvfp4_status_t status);
+
+/* Bytes of workspace nvfp4_quantize / nvfp4_kv_quantize need (amax partial
+ * maxima).  Never more than 4 KiB. */
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_quantize -- quantize x [rows][cols] (row stride ldx elements,
+ * dtype NVFP4_F32 or NVFP4_BF16) into NVFP4.
+ *   block  NVFP4_ROW16 (cols % 16 == 0), NVFP4_TILE16 (rows, cols % 16 == 0)
+ *          or NVFP4_COL16 (rows % 16 == 0).
+ *   rule   NVFP4_RULE_STATIC6 (block max -> 6) or NVFP4_RULE_4OVER6.
+ *   amax   NULL: the tensor's max |x| is computed on the device (one extra
+ *          read of x).  Otherwise a device pointer to a precomputed amax
+ *          (e.g. the same tensor's max used for another packing of it).
+ *   codes, scales, alpha: outputs as in the layout table above.
+ *   workspace: >= nvfp4_quantize_workspace_size(rows, cols) bytes (unused
+ *          when amax != NULL, may then be NULL).
+ * Source of the operation: "Hierarchical scaling" and "Quantization rule for a
+ * tensor block" (NVFP4 Training section) and "Scale-search mechanism" (NVFP4
+ * Inference section) of the architecture walkthrough page.
+ */
+nvfp4_status_t nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                              int block, int rule, const float *amax,
+                              uint8_t *codes, uint8_t *scales, float *alpha,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_dequantize -- y = (q * s) * alpha for a tensor packed by
+ * nvfp4_quantize with the same (rows, cols, block).  y is [rows][cols] in the
+ * ORIGINAL orientation (also for COL16), row stride ldy, dtype NVFP4_F32 or
+ * NVFP4_BF16 (bf16 = round-to-nearest-even of the fp32 value).
+ * Source: the "Hierarchical scaling" equation.
+ */
+nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha,
+                                int64_t rows, int64_t cols, int block,
+                                void *y, int y_dtype, int64_t ldy, hipStream_t stream);
+
+/*
+ * nvfp4_gemm -- C[m][n] = alpha_A * alpha_B * sum_k Ahat[m][k] * Bhat[n][k]
+ * (both operands K-contiguous, "NT"), fp32 accumulation, fp32 or bf16 out.
+ *   A: codes [m][k/2], scales 1D [m][k/16] or 2D [m/16][k/16], alpha.
+ *   B: codes [n][k/2], scales 1D [n][k/16] or 2D [n/16][k/16], alpha.
+ *   A ROW16 or TILE16 tensor of shape [r][k] is an operand as is; a COL16
+ *   tensor of x [k][r] is the operand x^T [r][k] with 1D scales.
+ *   k % 16 == 0; 2D scales need the operand's row count % 16 == 0.
+ *   C [m][n], row stride ldc, dtype NVFP4_F32 or NVFP4_BF16.
+ * The dequantized operands q*s are exact in fp16, so the contraction runs on
+ * fp16 MFMA with fp32 accumulation; accumulation order is unspecified.
+ * Source: "The three GEMMs of backpropagation" and "Quantization-
+ * dequantization flow" (NVFP4 Training section).
+ */
+nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha,
+                          int a_scale_layout,
+                          const uint8_t *b_codes, const uint8_t *b_scales, const float *b_alpha,
+                          int b_scale_layout,
+                          int64_t m, int64_t n, int64_t k,
+                          void *c, int c_dtype, int64_t ldc, hipStream_t stream);
+
+/*
+ * nvfp4_kv_quantize -- quantize one K or V cache tensor of `vectors` rows of
+ * head_dim elements (any leading-dimension order, e.g. [heads][tokens] or
+ * [tokens][heads], contiguous, so vectors = heads * tokens), 16-element
+ * blocks along head_dim, one alpha for the whole tensor.  Equivalent to
+ * nvfp4_quantize(kv, dtype, vectors, head_dim, head_dim, NVFP4_ROW16, rule,
+ * NULL, ...).  head_dim % 16 == 0.
+ * Source: "KV cache quantization" / "Chunkwise quantization procedure"
+ * (NVFP4 Inference section of the architecture walkthrough page).
+ */
+nvfp4_status_t nvfp4_kv_quantize(const void *kv, int kv_dtype, int64_t vectors, int64_t head_dim,
+                                 int rule, uint8_t *codes, uint8_t *scales, float *alpha,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace of nvfp4_linear: the packed activation (m*k*9/16 bytes) plus the
+ * amax partials, rounded up. */
+size_t nvfp4_linear_workspace_size(int64_t m, int64_t k);
+
+/*
+ * nvfp4_linear -- the W4A4 forward GEMM with activation quantization fused
+ * into the call: quantize x [m][k] (ROW16, `rule`, amax computed on the
+ * device) into the workspace, then y = nvfp4_gemm(x_packed, w).
+ *   w: packed weight [n][k] (TILE16 -> NVFP4_SCALE_2D, ROW16 -> _1D).
+ * Source: "Quantization-dequantization flow" (FPROP: weight x activation ->
+ * BF16 output).
+ */
+nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                            const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                            int w_scale_layout, int64_t n,
+                            void *y, int y_dtype, int64_t ldy,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace of nvfp4_wgrad: both COL16-packed operands plus amax partials. */
+size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in);
+
+/*
+ * nvfp4_wgrad -- weight gradient dW[n][k] = sum_t dY[t][n] * X[t][k] with
+ * both operands quantized in 16-blocks along the token axis (NVFP4_COL16,
+ * `rule`, amax of each computed on the device).  dy [tokens][n_out] (ld lddy),
+ * x [tokens][k_in] (ld ldx), same dtype; tokens % 16 == 0.  dW [n_out][k_in]
+ * (ld lddw), fp32 or bf16.
+ * Source: "The three GEMMs of backpropagation" (WGRAD: activation x output
+ * gradient -> weight gradient) with 1D gradient blocks along the reduction
+ * dimension ("NVFP4 training recipe").
+ */
+nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out,
+                           int64_t k_in, int64_t lddy, int64_t ldx, int rule,
+                           void *dw, int dw_dtype, int64_t lddw,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

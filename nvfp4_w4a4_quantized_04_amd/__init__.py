@@ -1,0 +1,264 @@
+"""MI355X-native NVFP4 W4A4 library -- Python binding of libnvfp4.so.
+
+Argument marshalling only: every step of the quantizer, the dequantizer and
+the GEMM runs in the HIP kernels behind the C ABI declared in
+``include/nvfp4.h``.  PyTorch provides device memory and the current stream.
+There is no CPU fallback: importing this module without the built library
+raises, and every call requires CUDA/HIP tensors.
+
+Names follow the pages ("LongLive-2.0: An NVFP4 Parallel Infrastructure for
+Long Video Generation": ``quantize_to_fp4`` / ``fp4_dequantize`` /
+``quantize_kv`` on the paper-notes page, section 3.4 and 3.6; the W4A4
+linear of the architecture walkthrough page, NVFP4 Inference section).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+F32, BF16 = 0, 1
+ROW16, TILE16, COL16 = 0, 1, 2
+STATIC6, FOUR_OVER_SIX = 0, 1
+SCALE_1D, SCALE_2D = 0, 1
+_BLOCKS = {"row16": ROW16, "tile16": TILE16, "col16": COL16}
+_RULES = {"static6": STATIC6, "static_6": STATIC6, "4over6": FOUR_OVER_SIX, "mse": FOUR_OVER_SIX}
+
+STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "alignment", 4: "dtype/enum", 5: "workspace", 6: "launch"}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({STATUS.get(status, '?')})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m nvfp4_w4a4_quantized_04_amd.build` "
+                          "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nvfp4_abi_version.restype = i32
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [i32]
+    L.nvfp4_quantize_workspace_size.restype = sz
+    L.nvfp4_quantize_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
+    L.nvfp4_dequantize.restype = i32
+    L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, i32, i64, P]
+    L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, P, i32, i64, P]
+    L.nvfp4_kv_quantize.restype = i32
+    L.nvfp4_kv_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, P, sz, P]
+    L.nvfp4_linear_workspace_size.restype = sz
+    L.nvfp4_linear_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_linear.restype = i32
+    L.nvfp4_linear.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, sz, P]
+    L.nvfp4_wgrad_workspace_size.restype = sz
+    L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
+    L.nvfp4_wgrad.restype = i32
+    L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, P, i32, i64, P, sz, P]
+    return L
+
+
+lib = _load()
+
+EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
+            "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
+            "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad"]
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise NVFP4Error(fn, st)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _out_dtype_code(d) -> int:
+    if d == torch.bfloat16:
+        return BF16
+    if d == torch.float32:
+        return F32
+    raise TypeError(f"unsupported output dtype {d}")
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("NVFP4 kernels need device tensors (no CPU fallback)")
+
+
+@dataclass
+class NVFP4Tensor:
+    """Packed NVFP4 tensor of logical shape [rows, cols].
+
+    codes: uint8 [rows, cols/2] (ROW16/TILE16) or [cols, rows/2] (COL16),
+    element 2j in the low nibble; scales: uint8 E4M3 bytes [rows, cols/16],
+    [rows/16, cols/16] or [cols, rows/16]; alpha: float32 [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    alpha: torch.Tensor
+    rows: int
+    cols: int
+    block: int
+
+    def operand(self):
+        """(codes, scales, alpha, scale layout, operand rows, K) for nvfp4_gemm."""
+        if self.block == COL16:
+            return self.codes, self.scales, self.alpha, SCALE_1D, self.cols, self.rows
+        return self.codes, self.scales, self.alpha, SCALE_2D if self.block == TILE16 else SCALE_1D, self.rows, self.cols
+
+
+def packed_shapes(rows: int, cols: int, block: int):
+    if block == ROW16:
+        return (rows, cols // 2), (rows, cols // 16)
+    if block == TILE16:
+        return (rows, cols // 2), (rows // 16, cols // 16)
+    return (cols, rows // 2), (cols, rows // 16)
+
+
+def empty_packed(rows: int, cols: int, block: int, device="cuda") -> NVFP4Tensor:
+    cs, ss = packed_shapes(rows, cols, block)
+    return NVFP4Tensor(torch.empty(cs, dtype=torch.uint8, device=device),
+                       torch.empty(ss, dtype=torch.uint8, device=device),
+                       torch.empty(1, dtype=torch.float32, device=device), rows, cols, block)
+
+
+def _block(block) -> int:
+    return _BLOCKS[block] if isinstance(block, str) else int(block)
+
+
+def _rule(rule) -> int:
+    return _RULES[rule] if isinstance(rule, str) else int(rule)
+
+
+def quantize(x: torch.Tensor, block="row16", rule="4over6", amax: torch.Tensor | None = None,
+             out: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """NVFP4-quantize a 2D float32/bfloat16 device tensor (``quantize_to_fp4``)."""
+    _need_gpu(x, amax)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2D with unit column stride")
+    b = _block(block)
+    rows, cols = x.shape
+    if out is None:
+        out = empty_packed(rows, cols, b, x.device)
+    if workspace is None and amax is None:
+        workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check("nvfp4_quantize", lib.nvfp4_quantize(
+        _ptr(x), _dtype_code(x), rows, cols, x.stride(0), b, _rule(rule), _ptr(amax),
+        _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), wsz, _stream()))
+    return out
+
+
+def dequantize(t: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Xhat = (q * s) * alpha in the tensor's original orientation (``fp4_dequantize``)."""
+    _need_gpu(t.codes)
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    _check("nvfp4_dequantize", lib.nvfp4_dequantize(
+        _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, t.block,
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
+    return out
+
+
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = alpha_A alpha_B Ahat Bhat^T on packed operands."""
+    ca, sa, aa, la, m, k = a.operand()
+    cb, sb, ab, lb, n, kb = b.operand()
+    if k != kb:
+        raise ValueError(f"contraction mismatch {k} vs {kb}")
+    _need_gpu(ca, cb)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=ca.device)
+    _check("nvfp4_gemm", lib.nvfp4_gemm(
+        _ptr(ca), _ptr(sa), _ptr(aa), la, _ptr(cb), _ptr(sb), _ptr(ab), lb, m, n, k,
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
+    return out
+
+
+def kv_quantize(kv: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """Quantize a K or V cache tensor [..., head_dim] (``quantize_kv``)."""
+    _need_gpu(kv)
+    if not kv.is_contiguous():
+        raise ValueError("kv must be contiguous")
+    d = kv.shape[-1]
+    vectors = kv.numel() // d if d else 0
+    if out is None:
+        out = empty_packed(vectors, d, ROW16, kv.device)
+    if workspace is None:
+        workspace = torch.empty(lib.nvfp4_quantize_workspace_size(vectors, d), dtype=torch.uint8, device=kv.device)
+    _check("nvfp4_kv_quantize", lib.nvfp4_kv_quantize(
+        _ptr(kv), _dtype_code(kv), vectors, d, _rule(rule), _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def linear_workspace(m: int, k: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib.nvfp4_linear_workspace_size(m, k), dtype=torch.uint8, device=device)
+
+
+def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4over6",
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 forward: y = quantize(x) @ w^T with the activation quantizer fused in the call."""
+    _need_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2D with unit column stride")
+    cw, sw, aw, lw, n, kw = w.operand()
+    m, k = x.shape
+    if k != kw:
+        raise ValueError(f"in_features mismatch {k} vs {kw}")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = linear_workspace(m, k, x.device)
+    _check("nvfp4_linear", lib.nvfp4_linear(
+        _ptr(x), _dtype_code(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n,
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def wgrad_workspace(tokens: int, n_out: int, k_in: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib.nvfp4_wgrad_workspace_size(tokens, n_out, k_in), dtype=torch.uint8, device=device)
+
+
+def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4over6",
+          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """dW = dY^T X with both operands NVFP4-quantized along the token axis."""
+    _need_gpu(dy, x)
+    t, n = dy.shape
+    t2, k = x.shape
+    if t != t2 or dy.dtype != x.dtype:
+        raise ValueError("dy and x need the same token count and dtype")
+    if out is None:
+        out = torch.empty((n, k), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = wgrad_workspace(t, n, k, x.device)
+    _check("nvfp4_wgrad", lib.nvfp4_wgrad(
+        _ptr(dy), _ptr(x), _dtype_code(x), t, n, k, dy.stride(0), x.stride(0), _rule(rule),
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+    return out

@@ -1,0 +1,270 @@
+// C ABI of libnvfp4.so: argument validation, workspace carving and launches.
+// Every entry point validates everything before enqueueing anything.
+#include <nvfp4.h>
+
+#include "internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;     // kernels index rows/cols with 32-bit ints in places
+constexpr size_t kAlignWs = 256;
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned_elem(const void *p, int dtype) { return ((uintptr_t)p & (dtype == NVFP4_BF16 ? 1u : 3u)) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool dtype_ok(int d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
+inline bool rule_ok(int r) { return r == NVFP4_RULE_STATIC6 || r == NVFP4_RULE_4OVER6; }
+inline bool block_ok(int b) { return b == NVFP4_ROW16 || b == NVFP4_TILE16 || b == NVFP4_COL16; }
+inline bool dims_ok(int64_t r, int64_t c) { return r >= 0 && c >= 0 && r < kMaxDim && c < kMaxDim; }
+
+nvfp4_status_t launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+// Shape rule of each block kind.
+bool block_shape_ok(int block, int64_t rows, int64_t cols)
+{
+    if (block == NVFP4_ROW16) return cols % 16 == 0;
+    if (block == NVFP4_TILE16) return rows % 16 == 0 && cols % 16 == 0;
+    return rows % 16 == 0;
+}
+
+nvfp4_status_t check_quant_args(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block,
+                                int rule, const uint8_t *codes, const uint8_t *scales, const float *alpha)
+{
+    if (!dtype_ok(x_dtype) || !rule_ok(rule) || !block_ok(block))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(rows, cols) || !block_shape_ok(block, rows, cols) || ldx < cols)
+        return NVFP4_ERR_SHAPE;
+    if (!alpha)
+        return NVFP4_ERR_NULL;
+    if (rows > 0 && cols > 0 && (!x || !codes || !scales))
+        return NVFP4_ERR_NULL;
+    // ROW16/TILE16 read x in 16-byte vectors; COL16 reads single elements
+    const bool vec = block != NVFP4_COL16;
+    if ((vec && (ldx % 8 != 0 || (x && !aligned16(x)))) || (x && !aligned_elem(x, x_dtype)) ||
+        (codes && !aligned16(codes)) || (scales && !aligned16(scales)))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// Quantize with the amax pass when no amax is given; ws holds the partials.
+nvfp4_status_t do_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
+                           const float *amax, uint8_t *codes, uint8_t *scales, float *alpha, float *partials,
+                           hipStream_t stream)
+{
+    const float *src = amax;
+    int n = 1;
+    if (!amax) {
+        n = amax_partials(rows, cols);
+        hipError_t e = launch_amax(x, x_dtype, rows, cols, ldx, partials, n, stream);
+        if (e != hipSuccess)
+            return NVFP4_ERR_LAUNCH;
+        src = partials;
+    }
+    return launch_status(launch_quantize(x, x_dtype, rows, cols, ldx, block, rule, src, n, codes, scales, alpha,
+                                         stream));
+}
+
+bool operand_ok(const uint8_t *codes, const uint8_t *scales, const float *alpha, int layout, int64_t rows,
+                int64_t k)
+{
+    (void)k;
+    if (layout != NVFP4_SCALE_1D && layout != NVFP4_SCALE_2D)
+        return false;
+    if (layout == NVFP4_SCALE_2D && rows % 16 != 0)
+        return false;
+    (void)codes; (void)scales; (void)alpha;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char *nvfp4_status_string(nvfp4_status_t s)
+{
+    switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case NVFP4_ERR_DTYPE: return "invalid dtype, block or rule";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols)
+{
+    (void)rows; (void)cols;
+    return kAmaxBytes;
+}
+
+nvfp4_status_t nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block,
+                              int rule, const float *amax, uint8_t *codes, uint8_t *scales, float *alpha,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    nvfp4_status_t st = check_quant_args(x, x_dtype, rows, cols, ldx, block, rule, codes, scales, alpha);
+    if (st != NVFP4_OK)
+        return st;
+    if (!amax) {
+        if (!workspace || workspace_bytes < nvfp4_quantize_workspace_size(rows, cols))
+            return NVFP4_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return NVFP4_ERR_ALIGN;
+    }
+    return do_quantize(x, x_dtype, rows, cols, ldx, block, rule, amax, codes, scales, alpha, (float *)workspace,
+                       stream);
+}
+
+nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                                int64_t cols, int block, void *y, int y_dtype, int64_t ldy, hipStream_t stream)
+{
+    if (!dtype_ok(y_dtype) || !block_ok(block))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(rows, cols) || !block_shape_ok(block, rows, cols) || ldy < cols)
+        return NVFP4_ERR_SHAPE;
+    if (rows > 0 && cols > 0 && (!codes || !scales || !alpha || !y))
+        return NVFP4_ERR_NULL;
+    const bool vec = block != NVFP4_COL16;       // ROW16/TILE16 write 16-byte vectors
+    if ((vec && (ldy % 8 != 0 || (y && !aligned16(y)))) || (y && !aligned_elem(y, y_dtype)) ||
+        (codes && !aligned16(codes)) || (scales && !aligned16(scales)))
+        return NVFP4_ERR_ALIGN;
+    return launch_status(launch_dequantize(codes, scales, alpha, rows, cols, block, y, y_dtype, ldy, stream));
+}
+
+nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha, int a_scale_layout,
+                          const uint8_t *b_codes, const uint8_t *b_scales, const float *b_alpha, int b_scale_layout,
+                          int64_t m, int64_t n, int64_t k, void *c, int c_dtype, int64_t ldc, hipStream_t stream)
+{
+    if (!dtype_ok(c_dtype))
+        return NVFP4_ERR_DTYPE;
+    if (!operand_ok(a_codes, a_scales, a_alpha, a_scale_layout, m, k) ||
+        !operand_ok(b_codes, b_scales, b_alpha, b_scale_layout, n, k))
+        return (a_scale_layout != 0 && a_scale_layout != 1) || (b_scale_layout != 0 && b_scale_layout != 1)
+                   ? NVFP4_ERR_DTYPE
+                   : NVFP4_ERR_SHAPE;
+    if (m < 0 || n < 0 || k < 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % 16 != 0 || ldc < n)
+        return NVFP4_ERR_SHAPE;
+    if (m > 0 && n > 0) {
+        if (!c || !a_alpha || !b_alpha)
+            return NVFP4_ERR_NULL;
+        if (k > 0 && (!a_codes || !a_scales || !b_codes || !b_scales))
+            return NVFP4_ERR_NULL;
+    }
+    if ((c && !aligned_elem(c, c_dtype)) || (a_codes && !aligned16(a_codes)) ||
+        (b_codes && !aligned16(b_codes)) || (a_scales && !aligned16(a_scales)) ||
+        (b_scales && !aligned16(b_scales)))
+        return NVFP4_ERR_ALIGN;
+    GemmOperand A{a_codes, a_scales, a_alpha, a_scale_layout};
+    GemmOperand B{b_codes, b_scales, b_alpha, b_scale_layout};
+    return launch_status(launch_gemm(A, B, m, n, k, c, c_dtype, ldc, stream));
+}
+
+nvfp4_status_t nvfp4_kv_quantize(const void *kv, int kv_dtype, int64_t vectors, int64_t head_dim, int rule,
+                                 uint8_t *codes, uint8_t *scales, float *alpha, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
+{
+    if (head_dim % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    return nvfp4_quantize(kv, kv_dtype, vectors, head_dim, head_dim, NVFP4_ROW16, rule, nullptr, codes, scales,
+                          alpha, workspace, workspace_bytes, stream);
+}
+
+// workspace: [alpha 256 B][amax partials][codes m*k/2][scales m*k/16]
+size_t nvfp4_linear_workspace_size(int64_t m, int64_t k)
+{
+    if (m < 0 || k < 0)
+        return 0;
+    return kAlignWs + round_up(kAmaxBytes, kAlignWs) + round_up((size_t)(m * k / 2), kAlignWs) +
+           round_up((size_t)(m * k / 16), kAlignWs);
+}
+
+nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                            const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                            int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype) || !rule_ok(rule) ||
+        (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n ||
+        (w_scale_layout == NVFP4_SCALE_2D && n % 16 != 0))
+        return NVFP4_ERR_SHAPE;
+    if (!w_alpha || (m > 0 && n > 0 && !y) || (m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!w_codes || !w_scales)))
+        return NVFP4_ERR_NULL;
+    if (ldx % 8 != 0 || (x && !aligned16(x)) || (y && !aligned_elem(y, y_dtype)) ||
+        (w_codes && !aligned16(w_codes)) || (w_scales && !aligned16(w_scales)))
+        return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
+        return NVFP4_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlignWs) != 0)
+        return NVFP4_ERR_ALIGN;
+    uint8_t *ws = (uint8_t *)workspace;
+    float *alpha = (float *)ws;
+    float *partials = (float *)(ws + kAlignWs);
+    uint8_t *codes = ws + kAlignWs + round_up(kAmaxBytes, kAlignWs);
+    uint8_t *scales = codes + round_up((size_t)(m * k / 2), kAlignWs);
+    nvfp4_status_t st = do_quantize(x, x_dtype, m, k, ldx, NVFP4_ROW16, rule, nullptr, codes, scales, alpha,
+                                    partials, stream);
+    if (st != NVFP4_OK)
+        return st;
+    GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};
+    GemmOperand B{w_codes, w_scales, w_alpha, w_scale_layout};
+    return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, stream));
+}
+
+// workspace: [alpha_dy][alpha_x] (256 B), [partials dy][partials x],
+//            [dy^T codes][dy^T scales][x^T codes][x^T scales]
+size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in)
+{
+    if (tokens < 0 || n_out < 0 || k_in < 0)
+        return 0;
+    return kAlignWs + 2 * round_up(kAmaxBytes, kAlignWs) + round_up((size_t)(n_out * tokens / 2), kAlignWs) +
+           round_up((size_t)(n_out * tokens / 16), kAlignWs) + round_up((size_t)(k_in * tokens / 2), kAlignWs) +
+           round_up((size_t)(k_in * tokens / 16), kAlignWs);
+}
+
+nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out, int64_t k_in,
+                           int64_t lddy, int64_t ldx, int rule, void *dw, int dw_dtype, int64_t lddw,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!dtype_ok(dtype) || !dtype_ok(dw_dtype) || !rule_ok(rule))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(tokens, n_out) || !dims_ok(k_in, 1) || tokens % 16 != 0 || lddy < n_out || ldx < k_in ||
+        lddw < k_in)
+        return NVFP4_ERR_SHAPE;
+    if ((n_out > 0 && k_in > 0 && !dw) || (tokens > 0 && ((n_out > 0 && !dy) || (k_in > 0 && !x))))
+        return NVFP4_ERR_NULL;
+    if ((dy && !aligned_elem(dy, dtype)) || (x && !aligned_elem(x, dtype)) || (dw && !aligned_elem(dw, dw_dtype)))
+        return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_wgrad_workspace_size(tokens, n_out, k_in))
+        return NVFP4_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlignWs) != 0)
+        return NVFP4_ERR_ALIGN;
+    uint8_t *ws = (uint8_t *)workspace;
+    float *alpha_dy = (float *)ws;
+    float *alpha_x = (float *)ws + 1;
+    float *part_dy = (float *)(ws + kAlignWs);
+    float *part_x = (float *)(ws + kAlignWs + round_up(kAmaxBytes, kAlignWs));
+    uint8_t *c_dy = ws + kAlignWs + 2 * round_up(kAmaxBytes, kAlignWs);
+    uint8_t *s_dy = c_dy + round_up((size_t)(n_out * tokens / 2), kAlignWs);
+    uint8_t *c_x = s_dy + round_up((size_t)(n_out * tokens / 16), kAlignWs);
+    uint8_t *s_x = c_x + round_up((size_t)(k_in * tokens / 2), kAlignWs);
+    nvfp4_status_t st = do_quantize(dy, dtype, tokens, n_out, lddy, NVFP4_COL16, rule, nullptr, c_dy, s_dy,
+                                    alpha_dy, part_dy, stream);
+    if (st != NVFP4_OK)
+        return st;
+    st = do_quantize(x, dtype, tokens, k_in, ldx, NVFP4_COL16, rule, nullptr, c_x, s_x, alpha_x, part_x, stream);
+    if (st != NVFP4_OK)
+        return st;
+    GemmOperand A{c_dy, s_dy, alpha_dy, NVFP4_SCALE_1D};
+    GemmOperand B{c_x, s_x, alpha_x, NVFP4_SCALE_1D};
+    return launch_status(launch_gemm(A, B, n_out, k_in, tokens, dw, dw_dtype, lddw, stream));
+}
+
+}  // extern "C"

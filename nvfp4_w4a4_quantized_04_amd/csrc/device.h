@@ -1,0 +1,180 @@
+// Device-side building blocks of the NVFP4 kernels for gfx950 (CDNA4).
+//
+// Format ("LongLive-2.0: An NVFP4 Parallel Infrastructure for Long Video
+// Generation", architecture walkthrough page, section "NVFP4 Training"):
+// E2M1 element codes, one E4M3 scale per 16-element block, one fp32 scale per
+// tensor, Xhat = X_FP4 * alpha_FP8 * alpha_FP32.
+//
+// Hardware conversions used (their rounding was checked against exact
+// references on the device):
+//   v_cvt_scalef32_pk_fp4_f32  fp32 pair -> E2M1 pair; with scale 1.0 it is
+//                              round-to-nearest-even, saturating at 6, and it
+//                              keeps the sign of zero (the scale operand only
+//                              contributes its exponent, so it is left at 1).
+//   v_cvt_scalef32_pk_f32_fp4  E2M1 pair -> fp32 pair, exact.
+//   v_cvt_scalef32_pk_f16_fp4  E2M1 pair -> fp16 pair, exact.
+//   v_cvt_pk_fp8_f32           fp32 pair -> E4M3FN pair, nearest-even with
+//                              subnormals; returns NaN above 464, so inputs are
+//                              clamped to 448 first (the saturating rule).
+//   v_cvt_f32_fp8 / v_cvt_scalef32_pk_f16_fp8  E4M3 -> fp32 / fp16, exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+// M_FP8 * M_FP4: the global scale maps the tensor max to 448 * 6.
+constexpr float kGlobalRange = 2688.0f;
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// alpha_FP32 from the tensor's absolute maximum.
+__device__ __forceinline__ float global_scale(float amax)
+{
+    return amax == 0.0f ? 1.0f : amax / kGlobalRange;
+}
+
+// Two E2M1 codes (a -> low nibble, b -> high nibble) into byte SEL of old.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_put2(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Values of the two codes in byte SEL of w.
+template <int SEL>
+__device__ __forceinline__ float2v e2m1_get2(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// E4M3 bytes of two non-negative values: byte 0 <- a, byte 1 <- b.
+__device__ __forceinline__ uint32_t e4m3_put2(float a, float b)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(a, kE4M3Max), fminf(b, kE4M3Max), 0, false) &
+           0xffffu;
+}
+
+template <int SEL>
+__device__ __forceinline__ float e4m3_get(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// One candidate encoding of a 16-element block row with block scale s:
+// codes of x * (1 / (s * alpha)) and the fma chain of squared errors of the
+// dequantized values (q * s) * alpha, continued from e.
+__device__ __forceinline__ void encode16(const float (&x)[16], float s, float alpha, uint32_t &c0,
+                                         uint32_t &c1, float &e)
+{
+    float kappa = 0.0f;
+    if (s != 0.0f) {
+        float d = s * alpha;
+        kappa = 1.0f / d;                 // IEEE division (correctly rounded)
+    }
+    uint32_t w0 = 0, w1 = 0;
+    w0 = e2m1_put2<0>(w0, x[0] * kappa, x[1] * kappa);
+    w0 = e2m1_put2<1>(w0, x[2] * kappa, x[3] * kappa);
+    w0 = e2m1_put2<2>(w0, x[4] * kappa, x[5] * kappa);
+    w0 = e2m1_put2<3>(w0, x[6] * kappa, x[7] * kappa);
+    w1 = e2m1_put2<0>(w1, x[8] * kappa, x[9] * kappa);
+    w1 = e2m1_put2<1>(w1, x[10] * kappa, x[11] * kappa);
+    w1 = e2m1_put2<2>(w1, x[12] * kappa, x[13] * kappa);
+    w1 = e2m1_put2<3>(w1, x[14] * kappa, x[15] * kappa);
+    float q[16];
+    float2v t;
+    t = e2m1_get2<0>(w0); q[0] = t[0]; q[1] = t[1];
+    t = e2m1_get2<1>(w0); q[2] = t[0]; q[3] = t[1];
+    t = e2m1_get2<2>(w0); q[4] = t[0]; q[5] = t[1];
+    t = e2m1_get2<3>(w0); q[6] = t[0]; q[7] = t[1];
+    t = e2m1_get2<0>(w1); q[8] = t[0]; q[9] = t[1];
+    t = e2m1_get2<1>(w1); q[10] = t[0]; q[11] = t[1];
+    t = e2m1_get2<2>(w1); q[12] = t[0]; q[13] = t[1];
+    t = e2m1_get2<3>(w1); q[14] = t[0]; q[15] = t[1];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        float xh = (q[i] * s) * alpha;
+        float d = x[i] - xh;
+        e = __builtin_fmaf(d, d, e);
+    }
+    c0 = w0;
+    c1 = w1;
+}
+
+// Quantize one 1D block of 16 values (RULE4: four-over-six).  Returns the
+// codes (8 bytes) and the E4M3 scale byte.
+template <bool RULE4>
+__device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha, uint32_t &c0,
+                                              uint32_t &c1, uint32_t &sbyte)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        m = fmaxf(m, fabsf(x[i]));
+    float mu = m / alpha;
+    float t6 = mu / 6.0f;
+    float t4 = mu * 0.25f;                 // == RN(mu / 4)
+    uint32_t sb = e4m3_put2(t6, t4);       // byte0: s6, byte1: s4
+    float s6 = e4m3_get<0>(sb);
+    float e6 = 0.0f;
+    encode16(x, s6, alpha, c0, c1, e6);
+    sbyte = sb & 0xffu;
+    if (RULE4) {
+        float s4 = e4m3_get<1>(sb);
+        uint32_t d0, d1;
+        float e4 = 0.0f;
+        encode16(x, s4, alpha, d0, d1, e4);
+        if (e4 < e6) {
+            c0 = d0;
+            c1 = d1;
+            sbyte = (sb >> 8) & 0xffu;
+        }
+    }
+}
+
+// 16 consecutive elements of row-major input (16-byte aligned).
+__device__ __forceinline__ void load16(const uint16_t *p, float (&x)[16])
+{
+    uint4 a = *reinterpret_cast<const uint4 *>(p);
+    uint4 b = *reinterpret_cast<const uint4 *>(p + 8);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+__device__ __forceinline__ void load16(const float *p, float (&x)[16])
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float4 v = *reinterpret_cast<const float4 *>(p + 4 * i);
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+    }
+}
+
+__device__ __forceinline__ float load1(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+
+// Wave-wide max (64 lanes).
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace nvfp4

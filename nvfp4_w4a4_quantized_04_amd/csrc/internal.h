@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+
+namespace nvfp4 {
+
+constexpr int kQuantThreads = 256;      // threads per quantize workgroup
+constexpr int kColGroups = 8;           // row-blocks per lane in the COL16 kernel
+constexpr int kMaxAmaxPartials = 1024;  // amax pass: at most this many workgroups
+constexpr size_t kAmaxBytes = kMaxAmaxPartials * sizeof(float);
+
+// number of amax workgroups (= partial maxima) for a rows x cols tensor
+int amax_partials(int64_t rows, int64_t cols);
+
+// dtype: 0 fp32, 1 bf16.  block: 0 ROW16, 1 TILE16, 2 COL16.
+hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
+                       int n_partials, hipStream_t s);
+
+// amax_src: n_amax partial maxima (n_amax > 1) or one amax (n_amax == 1).
+hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
+                           const float *amax_src, int n_amax, uint8_t *codes, uint8_t *scales, float *alpha,
+                           hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                             int64_t cols, int block, void *y, int ydtype, int64_t ldy, hipStream_t s);
+
+struct GemmOperand {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *alpha;
+    int scale2d;
+};
+
+hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
+                       int cdtype, int64_t ldc, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,417 @@
+// NVFP4 quantize / dequantize / amax kernels for gfx950.
+//
+// Operation ("LongLive-2.0: An NVFP4 Parallel Infrastructure for Long Video
+// Generation", architecture walkthrough page, NVFP4 Training section,
+// "Hierarchical scaling" and "Quantization rule for a tensor block"; NVFP4
+// Inference section, "Scale-search mechanism" and "Chunkwise quantization
+// procedure" for the KV cache):
+//   pass 1  amax of the tensor -> per-workgroup partial maxima
+//   pass 2  every workgroup reduces the partials (identical alpha everywhere),
+//           then each lane quantizes whole 16-element blocks held in its own
+//           registers: no cross-lane traffic on the hot path.
+#include "internal.h"
+
+namespace nvfp4 {
+
+// Reduce the partial maxima (or read one amax) into alpha; all threads of the
+// block get the same value.  Must be called by every thread of the block.
+__device__ __forceinline__ float block_alpha(const float *__restrict__ amax_src, int n_amax)
+{
+    __shared__ float red[kQuantThreads / 64];
+    float a = 0.0f;
+    if (n_amax == 1) {
+        a = amax_src[0];
+    } else {
+        for (int i = threadIdx.x; i < n_amax; i += kQuantThreads)
+            a = fmaxf(a, amax_src[i]);
+        a = wave_max(a);
+        if ((threadIdx.x & 63) == 0)
+            red[threadIdx.x >> 6] = a;
+        __syncthreads();
+        a = red[0];
+#pragma unroll
+        for (int w = 1; w < kQuantThreads / 64; w++)
+            a = fmaxf(a, red[w]);
+    }
+    return global_scale(a);
+}
+
+// ---------------------------------------------------------------- amax
+
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                        int64_t ldx, float *__restrict__ partials)
+{
+    __shared__ float red[kQuantThreads / 64];
+    float a = 0.0f;
+    if (ldx == cols) {
+        // contiguous: 16-byte vectors, grid-stride
+        constexpr int V = 16 / sizeof(T);
+        const int64_t n = rows * cols;
+        const int64_t nv = n / V;
+        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+        int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+        for (; i + 3 * stride < nv; i += 4 * stride) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[u] = reinterpret_cast<const uint4 *>(x)[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    if (sizeof(T) == 2) {
+                        a = fmaxf(a, fabsf(bf16_lo(w[j])));
+                        a = fmaxf(a, fabsf(bf16_hi(w[j])));
+                    } else {
+                        a = fmaxf(a, fabsf(__uint_as_float(w[j])));
+                    }
+                }
+            }
+        }
+        for (; i < nv; i += stride) {
+            uint4 v = reinterpret_cast<const uint4 *>(x)[i];
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                if (sizeof(T) == 2) {
+                    a = fmaxf(a, fabsf(bf16_lo(w[j])));
+                    a = fmaxf(a, fabsf(bf16_hi(w[j])));
+                } else {
+                    a = fmaxf(a, fabsf(__uint_as_float(w[j])));
+                }
+            }
+        }
+        for (int64_t t = nv * V + (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; t < n; t += stride)
+            a = fmaxf(a, fabsf(load1(x + t)));
+    } else {
+        // strided rows: one row per block iteration, threads along the row
+        for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+            for (int64_t c = threadIdx.x; c < cols; c += kQuantThreads)
+                a = fmaxf(a, fabsf(load1(x + r * ldx + c)));
+    }
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+#pragma unroll
+        for (int w = 1; w < kQuantThreads / 64; w++)
+            b = fmaxf(b, red[w]);
+        partials[blockIdx.x] = b;
+    }
+}
+
+// ------------------------------------------------------ ROW16 (1D, along cols)
+
+// One lane per 16-element block; blocks numbered row-major, so the codes of
+// block b are bytes [8b, 8b+8) and its scale is byte b (cols % 16 == 0).
+template <typename T, bool RULE4>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restrict__ x, int64_t rows, int64_t bpr,
+                                                               int64_t ldx, const float *__restrict__ amax_src,
+                                                               int n_amax, uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ scales,
+                                                               float *__restrict__ alpha_out)
+{
+    const float alpha = block_alpha(amax_src, n_amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *alpha_out = alpha;
+    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    if (b >= rows * bpr)
+        return;
+    const int64_t r = b / bpr;
+    const int64_t cb = b - r * bpr;
+    float v[16];
+    load16(x + r * ldx + cb * 16, v);
+    uint32_t c0, c1, sb;
+    quant_block16<RULE4>(v, alpha, c0, c1, sb);
+    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
+    scales[b] = (uint8_t)sb;
+}
+
+// ------------------------------------------------ COL16 (1D, along rows)
+
+// Blocks of 16 consecutive rows of one column.  Each lane owns one column and
+// walks kColGroups row-blocks; consecutive lanes take consecutive columns so
+// every row load of the wave is contiguous.  Output is the ROW16 packing of
+// x^T: codes [cols][rows/2], scales [cols][rows/16].
+template <typename T, bool RULE4>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                               int64_t ldx, const float *__restrict__ amax_src,
+                                                               int n_amax, uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ scales,
+                                                               float *__restrict__ alpha_out)
+{
+    const float alpha = block_alpha(amax_src, n_amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *alpha_out = alpha;
+    const int64_t c = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    if (c >= cols)
+        return;
+    const int64_t nrb = rows / 16;
+    for (int64_t rb0 = (int64_t)blockIdx.y * kColGroups; rb0 < nrb; rb0 += (int64_t)gridDim.y * kColGroups) {
+        for (int g = 0; g < kColGroups; g++) {
+            const int64_t rb = rb0 + g;
+            if (rb >= nrb)
+                break;
+            float v[16];
+            const T *p = x + rb * 16 * ldx + c;
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                v[i] = load1(p + i * ldx);
+            uint32_t c0, c1, sb;
+            quant_block16<RULE4>(v, alpha, c0, c1, sb);
+            *reinterpret_cast<uint2 *>(codes + c * (rows / 2) + rb * 8) = make_uint2(c0, c1);
+            scales[c * nrb + rb] = (uint8_t)sb;
+        }
+    }
+}
+
+// ---------------------------------------------------- TILE16 (16x16, weights)
+
+// Groups of 16 lanes own one tile; lane j of a group holds tile row j.  The
+// block error is the sum, in row order, of the per-row fma chains.
+template <typename T, bool RULE4>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                                int64_t ldx, const float *__restrict__ amax_src,
+                                                                int n_amax, uint8_t *__restrict__ codes,
+                                                                uint8_t *__restrict__ scales,
+                                                                float *__restrict__ alpha_out)
+{
+    const float alpha = block_alpha(amax_src, n_amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *alpha_out = alpha;
+    const int lane16 = threadIdx.x & 15;
+    const int64_t tb = (int64_t)blockIdx.x * (kQuantThreads / 16) + (threadIdx.x >> 4);   // tile column
+    const int64_t tpr = cols / 16;
+    // whole 16-lane groups leave together, so the shuffles below stay inside
+    // fully active groups
+    if (tb >= tpr)
+        return;
+    for (int64_t rb = blockIdx.y; rb < rows / 16; rb += gridDim.y) {     // tile row
+        const int64_t r = rb * 16 + lane16;
+        float v[16];
+        load16(x + r * ldx + tb * 16, v);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o, 16));
+        const float mu = m / alpha;
+        const uint32_t sb = e4m3_put2(mu / 6.0f, mu * 0.25f);
+        const float s6 = e4m3_get<0>(sb);
+        uint32_t c0, c1;
+        float er = 0.0f;
+        encode16(v, s6, alpha, c0, c1, er);
+        float e6 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            e6 = e6 + __shfl(er, i, 16);
+        uint32_t sbyte = sb & 0xffu;
+        if (RULE4) {
+            const float s4 = e4m3_get<1>(sb);
+            uint32_t d0, d1;
+            float er4 = 0.0f;
+            encode16(v, s4, alpha, d0, d1, er4);
+            float e4 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                e4 = e4 + __shfl(er4, i, 16);
+            if (e4 < e6) {
+                c0 = d0;
+                c1 = d1;
+                sbyte = (sb >> 8) & 0xffu;
+            }
+        }
+        *reinterpret_cast<uint2 *>(codes + r * (cols / 2) + tb * 8) = make_uint2(c0, c1);
+        if (lane16 == 0)
+            scales[rb * tpr + tb] = (uint8_t)sbyte;
+    }
+}
+
+// ------------------------------------------------------------ dequantize
+
+template <typename O>
+__device__ __forceinline__ void store1(O *p, float v);
+template <>
+__device__ __forceinline__ void store1<float>(float *p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store1<uint16_t>(uint16_t *p, float v)
+{
+    __bf16 h = (__bf16)v;                  // round to nearest even
+    *p = __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ void decode16(uint32_t c0, uint32_t c1, float s, float alpha, float (&y)[16])
+{
+    float2v t;
+    uint32_t w[2] = {c0, c1};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        t = e2m1_get2<0>(w[h]); y[8 * h + 0] = t[0]; y[8 * h + 1] = t[1];
+        t = e2m1_get2<1>(w[h]); y[8 * h + 2] = t[0]; y[8 * h + 3] = t[1];
+        t = e2m1_get2<2>(w[h]); y[8 * h + 4] = t[0]; y[8 * h + 5] = t[1];
+        t = e2m1_get2<3>(w[h]); y[8 * h + 6] = t[0]; y[8 * h + 7] = t[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        y[i] = (y[i] * s) * alpha;
+}
+
+// ROW16 / TILE16: one lane per 16-element row segment.
+template <typename O, bool TILE>
+__global__ __launch_bounds__(kQuantThreads) void k_dequant_rows(const uint8_t *__restrict__ codes,
+                                                                const uint8_t *__restrict__ scales,
+                                                                const float *__restrict__ alpha_p, int64_t rows,
+                                                                int64_t bpr, O *__restrict__ y, int64_t ldy)
+{
+    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    if (b >= rows * bpr)
+        return;
+    const float alpha = *alpha_p;
+    const int64_t r = b / bpr;
+    const int64_t cb = b - r * bpr;
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + b * 8);
+    const int64_t soff = TILE ? (r / 16) * bpr + cb : b;
+    const float s = e4m3_get<0>(scales[soff]);
+    float v[16];
+    decode16(c.x, c.y, s, alpha, v);
+    O *out = y + r * ldy + cb * 16;
+    if (sizeof(O) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            reinterpret_cast<float4 *>(out)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __bf16 lo = (__bf16)v[2 * i], hi = (__bf16)v[2 * i + 1];
+            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        reinterpret_cast<uint4 *>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+// COL16: lanes take consecutive columns of the original [rows][cols] tensor.
+template <typename O>
+__global__ __launch_bounds__(kQuantThreads) void k_dequant_col16(const uint8_t *__restrict__ codes,
+                                                                 const uint8_t *__restrict__ scales,
+                                                                 const float *__restrict__ alpha_p, int64_t rows,
+                                                                 int64_t cols, O *__restrict__ y, int64_t ldy)
+{
+    const int64_t idx = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    const int64_t nrb = rows / 16;
+    if (idx >= cols * nrb)
+        return;
+    const float alpha = *alpha_p;
+    const int64_t rb = idx / cols;
+    const int64_t c = idx - rb * cols;
+    const uint2 cw = *reinterpret_cast<const uint2 *>(codes + c * (rows / 2) + rb * 8);
+    const float s = e4m3_get<0>(scales[c * nrb + rb]);
+    float v[16];
+    decode16(cw.x, cw.y, s, alpha, v);
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        store1<O>(y + (rb * 16 + i) * ldy + c, v[i]);
+}
+
+// ------------------------------------------------------------ launchers
+
+int amax_partials(int64_t rows, int64_t cols)
+{
+    const int64_t n = rows * cols;
+    int64_t p = (n + (int64_t)kQuantThreads * 64 - 1) / ((int64_t)kQuantThreads * 64);
+    if (p < 1) p = 1;
+    if (p > kMaxAmaxPartials) p = kMaxAmaxPartials;
+    return (int)p;
+}
+
+hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
+                       int n_partials, hipStream_t s)
+{
+    if (dtype == 1)
+        k_amax<uint16_t><<<n_partials, kQuantThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, partials);
+    else
+        k_amax<float><<<n_partials, kQuantThreads, 0, s>>>((const float *)x, rows, cols, ldx, partials);
+    return hipGetLastError();
+}
+
+template <typename T, bool R4>
+static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, int block, const float *amax_src,
+                           int n_amax, uint8_t *codes, uint8_t *scales, float *alpha, hipStream_t s)
+{
+    if (block == 0) {
+        const int64_t bpr = cols / 16;
+        const int64_t nb = rows * bpr;
+        const unsigned grid = (unsigned)((nb + kQuantThreads - 1) / kQuantThreads);
+        k_quant_row16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
+    } else if (block == 1) {
+        const int64_t tpr = cols / 16;
+        const int64_t ty = rows / 16 < 65535 ? rows / 16 : 65535;
+        dim3 grid((unsigned)((tpr + kQuantThreads / 16 - 1) / (kQuantThreads / 16)), (unsigned)ty);
+        k_quant_tile16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha);
+    } else {
+        const int64_t nrb = rows / 16;
+        int64_t gy = (nrb + kColGroups - 1) / kColGroups;
+        if (gy > 65535) gy = 65535;
+        dim3 grid((unsigned)((cols + kQuantThreads - 1) / kQuantThreads), (unsigned)gy);
+        k_quant_col16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha);
+    }
+}
+
+hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
+                           const float *amax_src, int n_amax, uint8_t *codes, uint8_t *scales, float *alpha,
+                           hipStream_t s)
+{
+    if (rows == 0 || cols == 0) {
+        // nothing to encode; alpha still follows the rule (amax 0 -> 1)
+        k_quant_row16<float, false><<<1, kQuantThreads, 0, s>>>(nullptr, 0, 0, 0, amax_src, n_amax, codes, scales,
+                                                                alpha);
+        return hipGetLastError();
+    }
+    if (dtype == 1) {
+        if (rule) launch_quant_t<uint16_t, true>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+        else      launch_quant_t<uint16_t, false>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+    } else {
+        if (rule) launch_quant_t<float, true>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+        else      launch_quant_t<float, false>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                             int64_t cols, int block, void *y, int ydtype, int64_t ldy, hipStream_t s)
+{
+    if (rows == 0 || cols == 0)
+        return hipSuccess;
+    if (block == 2) {
+        const int64_t n = cols * (rows / 16);
+        const unsigned grid = (unsigned)((n + kQuantThreads - 1) / kQuantThreads);
+        if (ydtype == 1)
+            k_dequant_col16<uint16_t><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, cols, (uint16_t *)y, ldy);
+        else
+            k_dequant_col16<float><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, cols, (float *)y, ldy);
+    } else {
+        const int64_t bpr = cols / 16;
+        const unsigned grid = (unsigned)((rows * bpr + kQuantThreads - 1) / kQuantThreads);
+        if (block == 1) {
+            if (ydtype == 1)
+                k_dequant_rows<uint16_t, true><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, bpr, (uint16_t *)y, ldy);
+            else
+                k_dequant_rows<float, true><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, bpr, (float *)y, ldy);
+        } else {
+            if (ydtype == 1)
+                k_dequant_rows<uint16_t, false><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, bpr, (uint16_t *)y, ldy);
+            else
+                k_dequant_rows<float, false><<<grid, kQuantThreads, 0, s>>>(codes, scales, alpha, rows, bpr, (float *)y, ldy);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4
