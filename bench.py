@@ -1,0 +1,269 @@
+"""Benchmark of the NVFP4 W4A4 hot path on one MI355X.
+
+One step = one W4A4 linear of the QKV projection of a 5B video DiT block:
+activation amax + NVFP4 quantization of X bf16 [2640, 3072] + NVFP4 GEMM
+against the pre-quantized weight W [9216, 3072] (16x16 tiles, four-over-six)
+with fp32 accumulation and bf16 output -- one call of nvfp4_linear.
+`value` is its throughput in TFLOP/s (2*M*N*K per step), inputs resident in
+device memory, three rotating input/weight sets.
+
+The same JSON line also carries
+  roofline      the GEMM kernel alone, timed with HIP events on its stream,
+                against the fp16 MFMA peak (its operands are exact fp16);
+  kv            NVFP4 KV-cache quantize and dequantize of K and V bf16
+                [24, 18480, 128] in GB/s of algorithmic bytes, and against HBM;
+  extra         the FFN pair and the long-sequence training shapes;
+  cpu_baseline  the CPU oracle (fp32 quantizer, fp64 GEMM) on the full QKV
+                step on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A4 GEMM TFLOPS incl. act-quantize at DiT shapes; KV-quantize GB/s"
+HBM_PEAK_GBPS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0       # dense fp16/bf16 MFMA, MI355X
+FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def time_events(fn, iters: int, warmup: int = 3) -> float:
+    """Average milliseconds per call of fn() measured with events on the
+    current stream (where the library enqueues)."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def linear_sets(nv, workloads, m, k, n, nsets, seed0):
+    """Rotating (x, packed W, y, workspace) sets for one linear shape."""
+    import torch
+    sets = []
+    for i in range(nsets):
+        c = workloads.config2(seed=seed0 + 100 * i, m=m, k=k, n=n)
+        x = dev_bf16(c["x"])
+        w = nv.quantize(dev_bf16(c["w"]), "tile16", "4over6")
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = nv.linear_workspace(m, k)
+        sets.append((x, w, y, ws))
+    torch.cuda.synchronize()
+    return sets
+
+
+def bench_linear(nv, sets, steps, warmup):
+    import torch
+
+    def step(i):
+        x, w, y, ws = sets[i % len(sets)]
+        nv.linear(x, w, torch.bfloat16, out=y, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def bench_gemm_kernel(nv, sets, iters):
+    """The GEMM kernel alone on pre-quantized activations (events)."""
+    import torch
+    packed = []
+    for x, w, y, ws in sets:
+        packed.append((nv.quantize(x, "row16", "4over6"), w, y))
+    torch.cuda.synchronize()
+
+    def call(i):
+        a, w, y = packed[i % len(packed)]
+        nv.gemm(a, w, torch.bfloat16, out=y)
+
+    return time_events(call, iters)
+
+
+def bench_kv(nv, workloads, iters):
+    import torch
+    c = workloads.config4()
+    heads, tokens, d = c["k"].shape
+    n = heads * tokens * d
+    sets = []
+    for name in ("k", "v"):
+        t = dev_bf16(c[name])
+        sets.append((t, nv.empty_packed(heads * tokens, d, nv.ROW16),
+                     torch.empty((heads * tokens, d), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty(nv.lib.nvfp4_quantize_workspace_size(heads * tokens, d), dtype=torch.uint8,
+                                 device="cuda")))
+    # a third pair of buffers so consecutive calls never hit the same data in
+    # the 256 MB last-level cache
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    extra = torch.randn((heads, tokens, d), generator=g, device="cuda").to(torch.bfloat16)
+    sets.append((extra, nv.empty_packed(heads * tokens, d, nv.ROW16),
+                 torch.empty((heads * tokens, d), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty(nv.lib.nvfp4_quantize_workspace_size(heads * tokens, d), dtype=torch.uint8,
+                             device="cuda")))
+    torch.cuda.synchronize()
+
+    def q(i):
+        kv, p, y, ws = sets[i % len(sets)]
+        nv.kv_quantize(kv, "4over6", out=p, workspace=ws)
+
+    def dq(i):
+        kv, p, y, ws = sets[i % len(sets)]
+        nv.dequantize(p, torch.bfloat16, out=y)
+
+    for i in range(len(sets)):
+        q(i)
+    tq = time_events(q, iters)
+    tdq = time_events(dq, iters)
+    bytes_q = n * 2 + n * 9 / 16 + 4          # read bf16, write codes + scales + alpha
+    bytes_dq = n * 9 / 16 + 4 + n * 2
+    return {
+        "workload": f"K/V bf16 [{heads},{tokens},{d}], 16-blocks along head_dim, four-over-six",
+        "quantize_ms_per_tensor": round(tq, 5),
+        "quantize_GBps": round(bytes_q / (tq * 1e-3) / 1e9, 1),
+        "quantize_frac_hbm": round(bytes_q / (tq * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "dequantize_ms_per_tensor": round(tdq, 5),
+        "dequantize_GBps": round(bytes_dq / (tdq * 1e-3) / 1e9, 1),
+        "dequantize_frac_hbm": round(bytes_dq / (tdq * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
+        "note": "quantize includes the amax pass; GB/s = algorithmic bytes / event time per call",
+    }
+
+
+def bench_extra(nv, workloads, iters):
+    """FFN pair and long-sequence training shapes (fused act-quantize + GEMM)."""
+    import torch
+    out = {}
+    for name, (m, k, n) in {"ffn_up_m2640_k3072_n14336": (2640, 3072, 14336),
+                            "ffn_down_m2640_k14336_n3072": (2640, 14336, 3072),
+                            "train_fwd_m32768_k3072_n3072": (32768, 3072, 3072)}.items():
+        sets = linear_sets(nv, workloads, m, k, n, 2, 30)
+        ms = bench_linear(nv, sets, iters, 3)
+        out[name] = {"ms": round(ms, 4), "TFLOPs": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+        del sets
+        torch.cuda.empty_cache()
+    # weight gradient dW = dY^T X over 32768 tokens
+    t, n, k = 32768, 3072, 3072
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    x = torch.randn((t, k), generator=g, device="cuda").to(torch.bfloat16)
+    dy = (torch.randn((t, n), generator=g, device="cuda") * 1e-3).to(torch.bfloat16)
+    dw = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+    ws = nv.wgrad_workspace(t, n, k)
+
+    def wg(i):
+        nv.wgrad(dy, x, torch.bfloat16, out=dw, workspace=ws)
+
+    ms = time_events(wg, iters)
+    out["train_wgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
+                                             "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    return out
+
+
+def cpu_baseline(workloads, m, k, n):
+    """The oracle (fp32 quantizer, fp64 GEMM, OpenMP) on the full QKV step."""
+    import oracle
+    c = workloads.config2()
+    W = oracle.quantize(c["w"], oracle.TILE16, oracle.FOUR_OVER_SIX)     # offline, untimed
+    t0 = time.perf_counter()
+    A = oracle.quantize(c["x"], oracle.ROW16, oracle.FOUR_OVER_SIX)
+    oracle.gemm_f64(A, W)
+    dt = time.perf_counter() - t0
+    return {"value": round(2 * m * n * k / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "full QKV step: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and the "
+                      "fp64 GEMM against W [9216,3072]"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-kv", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the NVFP4 path here is built and timed on a single MI355X "
+              "(multi-GPU sharding is a design note, not a measured run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_w4a4_quantized_04_amd as nv
+    import workloads
+
+    assert torch.cuda.is_available()
+    m, k, n = 2640, 3072, 9216
+    log("[bench] preparing QKV projection inputs")
+    sets = linear_sets(nv, workloads, m, k, n, 3, 2)
+    log("[bench] timing the fused linear")
+    ms = bench_linear(nv, sets, args.steps, args.warmup)
+    flops = 2.0 * m * n * k
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] linear {ms:.4f} ms/step, {value:.1f} TFLOP/s")
+
+    log("[bench] timing the GEMM kernel alone")
+    gms = bench_gemm_kernel(nv, sets, max(50, args.steps // 2))
+    achieved = flops / (gms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "k_gemm_nvfp4", "kernel_ms": round(gms, 5),
+                "frac_of_fp4_mfma_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4)}
+    del sets
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "nvfp4 operands, f16 mfma (exact), f32 accumulate, bf16 out",
+        "data": "synthetic (seeded normals shaped like a 5B video DiT's QKV projection)",
+        "config": {"workload": "qkv_projection_x2640x3072_w9216x3072_bf16out",
+                   "m": m, "k": k, "n": n, "rule": "four-over-six", "weight_blocks": "16x16",
+                   "act_blocks": "1x16"},
+        "roofline": roofline,
+    }
+    if not args.no_kv:
+        log("[bench] KV cache quantize/dequantize")
+        result["kv"] = bench_kv(nv, workloads, 30)
+        torch.cuda.empty_cache()
+    if not args.no_extra:
+        log("[bench] FFN and training shapes")
+        result["extra"] = bench_extra(nv, workloads, 20)
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(workloads, m, k, n)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
