@@ -6,28 +6,32 @@
 // dequantization flow") runs on Blackwell FP4 tensor cores with E4M3 block
 // scales.  gfx950's scaled FP4 MFMA only takes power-of-two (E8M0) scales per
 // 32 elements, so it cannot carry an E4M3 scale per 16 elements exactly.
-// Instead, every dequantized operand value q*s has at most 6 significant
-// bits and lies in [2^-10, 2688], so it is EXACT in fp16.  The kernel
-// therefore
-//   1. stages the packed operands (0.5 B codes + 1/16 B scales per element)
-//      from HBM into LDS, double buffered;
-//   2. each wave decodes its MFMA fragments with v_cvt_scalef32_pk_f16_fp4
-//      (exact) and one v_pk_mul_f16 by the block scale (exact);
-//   3. accumulates with v_mfma_f32_32x32x16_f16 in fp32;
-//   4. multiplies by alpha_A * alpha_B in the epilogue and stores fp32/bf16.
+// Every dequantized operand value q*s, however, has at most 6 significant
+// bits and lies in [2^-10, 2688]: it is EXACT in fp16, and fp16 MFMA runs at
+// the dense bf16 rate.  So the packed operands are decoded on chip and
+// contracted with v_mfma_f32_32x32x16_f16 (fp32 accumulation).
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid, each wave TM x TN MFMA tiles
-// of 32x32, so a workgroup tile is (64 TM) x (64 TN) with BK = 64 (four
-// 16-element scale blocks).  K order inside a BK step: lanes 0-31 of a
-// fragment hold k in [0, 32) and lanes 32-63 k in [32, 64) of the step, 8 per
-// MFMA; A and B use the same assignment, so the sum is over every k once.
+// Workgroup = 8 waves, two per SIMD, specialised:
+//   producers (waves 4-7) fetch packed stages (0.5 B codes + 1/16 B scale per
+//     element) from HBM PD steps ahead into registers, decode them with
+//     v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16 by the E4M3 block scale (both
+//     exact) and write fp16 tiles into LDS (double buffered, rows padded to
+//     144 B so 16 consecutive rows hit distinct banks);
+//   consumers (waves 0-3, 2x2 grid) hold the fp32 accumulators, read MFMA
+//     fragments from LDS one 16-k substep ahead and issue the MFMAs.
+// The decode VALU work of one wave then overlaps the MFMA work of the other
+// wave on the same SIMD.  One barrier per 64-k step hands a stage over.
+// Workgroup tile (64 TM) x (64 TN), BK = 64; consumer wave tile (32 TM) x (32 TN).
 #include "internal.h"
+
+#include <type_traits>
 
 namespace nvfp4 {
 
-constexpr int kBK = 64;             // K elements per main-loop step
-constexpr int kRowBytes = kBK / 2;  // code bytes per row per step
-constexpr int kLdsStride = 48;      // padded LDS row stride (bank-conflict free 16 B reads)
+constexpr int kBK = 64;                  // K elements per main-loop step
+constexpr int kRowBytes = kBK / 2;       // packed code bytes per row per step
+constexpr int kLdsRow = kBK * 2 + 16;    // fp16 LDS row: 128 B + 16 B pad
+constexpr int kPrefetch = 4;             // packed stages a producer holds in registers
 
 struct GemmArgs {
     const uint8_t *a_codes, *a_scales;
@@ -37,127 +41,201 @@ struct GemmArgs {
     int64_t ldc;
     int M, N, K;
     int a2d, b2d;
-    int tiles_n;
+    int tiles_m, tiles_n;
     int c_bf16;
+    int vec_ok;     // C pointer and ldc allow 4-element vector stores
 };
 
-template <int ROWS>
-struct StageRegs {
-    uint4 codes[(2 * ROWS + 255) / 256];
-    uint32_t scales[(ROWS + 255) / 256];
-};
-
-// Global -> registers for one operand tile of ROWS rows at K-step kt.
-template <int ROWS>
-__device__ __forceinline__ void load_stage(StageRegs<ROWS> &r, const uint8_t *__restrict__ codes,
-                                           const uint8_t *__restrict__ scales, int s2d, int row0, int nrows,
-                                           int K, int kt, bool kfull)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
 {
-    const int tid = threadIdx.x;
-    const int64_t rb = K / 2;       // code bytes per row
-    const int64_t sb = K / 16;      // scale bytes per scale row
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// A producer thread's share of one operand tile: "chunks" of 32 k values
+// (16 code bytes + 2 scale bytes) of one row; 2 chunks per row and step.
+template <int ROWS, bool KFULL, int NSLOT>
+struct Producer {
+    static constexpr int kTotal = 2 * ROWS;
+    static constexpr int kPer = (kTotal + 255) / 256;
+    uint32_t code_off[kPer];    // byte offset of the chunk in the code array at step 0
+    uint32_t scale_off[kPer];
+    uint32_t lds_off[kPer];
+    int ch_off[kPer];           // 0 or 16: the chunk's byte offset inside a step
+    uint4 codes[NSLOT][kPer];
+    uint32_t scales[NSLOT][kPer];
+    int rb;                     // code bytes per row (K/2)
+
+    __device__ __forceinline__ void init(int ptid, int s2d, int row0, int nrows, int K)
+    {
+        rb = K / 2;
+        const int sb = K / 16;
 #pragma unroll
-    for (int i = 0; i < (2 * ROWS + 255) / 256; i++) {
-        const int q = tid + 256 * i;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (q < 2 * ROWS) {
+        for (int i = 0; i < kPer; i++) {
+            int q = ptid + 256 * i;
+            q = q < kTotal ? q : kTotal - 1;        // extra threads repeat the last chunk (same data, same place)
             const int row = q >> 1, ch = q & 1;
-            const int gr = row0 + row;
-            if (gr < nrows) {
-                const int64_t off = (int64_t)gr * rb + (int64_t)kt * kRowBytes + ch * 16;
-                if (kfull) {
-                    v = *reinterpret_cast<const uint4 *>(codes + off);
-                } else {
-                    const int64_t left = rb - ((int64_t)kt * kRowBytes + ch * 16);
-                    if (left >= 8) {
-                        uint2 lo = *reinterpret_cast<const uint2 *>(codes + off);
-                        v.x = lo.x; v.y = lo.y;
-                    }
-                    if (left >= 16) {
-                        uint2 hi = *reinterpret_cast<const uint2 *>(codes + off + 8);
-                        v.z = hi.x; v.w = hi.y;
-                    }
+            int gr = row0 + row;
+            gr = gr < nrows ? gr : nrows - 1;       // rows past the end re-read the last row; never stored
+            const int srow = s2d ? gr / 16 : gr;
+            code_off[i] = (uint32_t)gr * (uint32_t)rb + ch * 16;
+            scale_off[i] = (uint32_t)srow * (uint32_t)sb + ch * 2;
+            lds_off[i] = row * kLdsRow + ch * 64;
+            ch_off[i] = ch * 16;
+        }
+    }
+
+    template <int SLOT>
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ cbase, const uint8_t *__restrict__ sbase,
+                                         int kt)
+    {
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            const uint32_t off = code_off[i] + (uint32_t)kt * kRowBytes;
+            const uint32_t soff = scale_off[i] + (uint32_t)kt * 4;
+            if (KFULL) {
+                codes[SLOT][i] = *reinterpret_cast<const uint4 *>(cbase + off);
+                scales[SLOT][i] = *reinterpret_cast<const uint16_t *>(sbase + soff);
+            } else {
+                // K % 64 != 0: codes past K read as zero (their scale is then irrelevant)
+                uint4 v = make_uint4(0, 0, 0, 0);
+                uint32_t s = 0;
+                const int pos = kt * kRowBytes + ch_off[i];
+                if (pos + 8 <= rb) {
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(cbase + off);
+                    v.x = lo.x; v.y = lo.y;
+                    s = sbase[soff];
                 }
+                if (pos + 16 <= rb) {
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(cbase + off + 8);
+                    v.z = hi.x; v.w = hi.y;
+                    s |= (uint32_t)sbase[soff + 1] << 8;
+                }
+                codes[SLOT][i] = v;
+                scales[SLOT][i] = s;
             }
         }
-        r.codes[i] = v;
     }
+
+    // decode the chunks of register slot SLOT and write them as fp16 to LDS
+    template <int SLOT>
+    __device__ __forceinline__ void store(uint8_t *lds) const
+    {
 #pragma unroll
-    for (int i = 0; i < (ROWS + 255) / 256; i++) {
-        const int row = tid + 256 * i;
-        uint32_t w = 0;
-        if (row < ROWS) {
-            const int gr = row0 + row;
-            if (gr < nrows) {
-                const int64_t srow = s2d ? gr / 16 : gr;
-                const int64_t off = srow * sb + (int64_t)kt * 4;
-                if (kfull) {
-                    w = *reinterpret_cast<const uint32_t *>(scales + off);
-                } else {
-                    const int64_t left = sb - (int64_t)kt * 4;
+        for (int i = 0; i < kPer; i++) {
+            const half2v s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales[SLOT][i], 1.0f, false);
+            const half2v lo = {s2[0], s2[0]};
+            const half2v hi = {s2[1], s2[1]};
+            const uint32_t w[4] = {codes[SLOT][i].x, codes[SLOT][i].y, codes[SLOT][i].z, codes[SLOT][i].w};
+            uint4 *dst = reinterpret_cast<uint4 *>(lds + lds_off[i]);
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        if (j < left)
-                            w |= (uint32_t)scales[off + j] << (8 * j);
-                }
+            for (int j = 0; j < 4; j++) {
+                const half2v sc = j < 2 ? lo : hi;       // code dwords 0-1: first 16-block, 2-3: second
+                const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 0) * sc;
+                const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 1) * sc;
+                const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 2) * sc;
+                const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[j], 1.0f, 3) * sc;
+                dst[j] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
             }
         }
-        r.scales[i] = w;
     }
-}
-
-template <int ROWS>
-__device__ __forceinline__ void store_stage(const StageRegs<ROWS> &r, uint8_t *lds_codes, uint32_t *lds_scales)
-{
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < (2 * ROWS + 255) / 256; i++) {
-        const int q = tid + 256 * i;
-        if (q < 2 * ROWS)
-            *reinterpret_cast<uint4 *>(lds_codes + (q >> 1) * kLdsStride + (q & 1) * 16) = r.codes[i];
-    }
-#pragma unroll
-    for (int i = 0; i < (ROWS + 255) / 256; i++) {
-        const int row = tid + 256 * i;
-        if (row < ROWS)
-            lds_scales[row] = r.scales[i];
-    }
-}
-
-// 8 fp16 operand values (exact q*s) from one code dword and a block scale.
-__device__ __forceinline__ half8v dequant8(uint32_t w, _Float16 s)
-{
-    const half2v ss = {s, s};
-    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    half8v o = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    return o;
-}
+};
 
 template <int TM, int TN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__device__ __forceinline__ void read_frags(const uint8_t *stage, const int (&a_frag)[TM], const int (&b_frag)[TN],
+                                           int s, half8v (&af)[TM], half8v (&bf)[TN])
+{
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+        af[i] = *reinterpret_cast<const half8v *>(stage + a_frag[i] + s * 32);
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+        bf[j] = *reinterpret_cast<const half8v *>(stage + b_frag[j] + s * 32);
+}
+
+template <int TM, int TN, bool KFULL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_nvfp4(GemmArgs g)
 {
     constexpr int BM = 64 * TM, BN = 64 * TN;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kLdsStride];
-    __shared__ uint32_t lds_as[2][BM];
-    __shared__ uint32_t lds_bs[2][BN];
+    constexpr int kStage = (BM + BN) * kLdsRow;
+    constexpr int PD = kPrefetch;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int wave = tid >> 6;
+
+    // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+    // L2.  Renumber so consecutive logical ids run on one XCD, then walk the
+    // tiles down a column (tm fastest) so an XCD shares weight tiles.
+    const int nwg = g.tiles_m * g.tiles_n;
+    const int per_xcd = (nwg + 7) / 8;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int full = nwg - (per_xcd - 1) * 8;              // XCDs that host per_xcd workgroups
+    const int lid = xcd < full ? xcd * per_xcd + idx : full * per_xcd + (xcd - full) * (per_xcd - 1) + idx;
+    const int tn = lid / g.tiles_m;
+    const int tm = lid - tn * g.tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (g.K + kBK - 1) / kBK;
+
+    if (wave >= 4) {
+        // ------------------------------------------------------ producers
+        // Stage j lives in register slot j % PD.  Step kt decodes stage kt+1
+        // into LDS buffer (kt+1)&1, then refills its slot with stage kt+1+PD.
+        Producer<BM, KFULL, PD> pa;
+        Producer<BN, KFULL, PD> pb;
+        const int ptid = tid - 256;
+        pa.init(ptid, g.a2d, m0, g.M, g.K);
+        pb.init(ptid, g.b2d, n0, g.N, g.K);
+        if (nk > 0) {
+            static_for<0, PD>([&](auto c) {
+                constexpr int S = decltype(c)::value;
+                const int ks = S < nk ? S : nk - 1;         // clamped: a repeated fetch is harmless
+                pa.template load<S>(g.a_codes, g.a_scales, ks);
+                pb.template load<S>(g.b_codes, g.b_scales, ks);
+            });
+            pa.template store<0>(lds);
+            pb.template store<0>(lds + BM * kLdsRow);
+            const int kp = PD < nk ? PD : nk - 1;
+            pa.template load<0>(g.a_codes, g.a_scales, kp);
+            pb.template load<0>(g.b_codes, g.b_scales, kp);
+        }
+        __syncthreads();
+        auto pstep = [&](int kt, auto slot_tag) {
+            constexpr int NS = decltype(slot_tag)::value;
+            uint8_t *nxt = lds + ((kt + 1) & 1) * kStage;
+            pa.template store<NS>(nxt);
+            pb.template store<NS>(nxt + BM * kLdsRow);
+            const int kf = kt + 1 + PD < nk ? kt + 1 + PD : nk - 1;
+            pa.template load<NS>(g.a_codes, g.a_scales, kf);
+            pb.template load<NS>(g.b_codes, g.b_scales, kf);
+            __syncthreads();
+        };
+        int kt = 0;
+        for (; kt + PD < nk; kt += PD)
+            static_for<0, PD>([&](auto c) {
+                constexpr int S = decltype(c)::value;
+                pstep(kt + S, std::integral_constant<int, (S + 1) % PD>{});
+            });
+        static_for<0, PD>([&](auto c) {
+            constexpr int S = decltype(c)::value;
+            if (kt + S + 1 < nk)
+                pstep(kt + S, std::integral_constant<int, (S + 1) % PD>{});
+            else if (kt + S < nk)
+                __syncthreads();              // matches the consumers' last step
+        });
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    const int lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int half = lane >> 5;
     const int l32 = lane & 31;
-
-    const int tm = blockIdx.x / g.tiles_n;
-    const int tn = blockIdx.x - tm * g.tiles_n;
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (g.K + kBK - 1) / kBK;
-    const bool kfull = (g.K % kBK) == 0;
 
     float16v acc[TM][TN];
 #pragma unroll
@@ -166,101 +244,125 @@ void k_gemm_nvfp4(GemmArgs g)
         for (int j = 0; j < TN; j++)
             acc[i][j] = float16v{};
 
-    StageRegs<BM> ra;
-    StageRegs<BN> rb;
-    if (nk > 0) {
-        load_stage<BM>(ra, g.a_codes, g.a_scales, g.a2d, m0, g.M, g.K, 0, kfull);
-        load_stage<BN>(rb, g.b_codes, g.b_scales, g.b2d, n0, g.N, g.K, 0, kfull);
-        store_stage<BM>(ra, lds_a[0], lds_as[0]);
-        store_stage<BN>(rb, lds_b[0], lds_bs[0]);
-    }
-    __syncthreads();
+    // fragment of MFMA tile i: LDS row (tile row + lane%32), k half (lane/32)
+    int a_frag[TM], b_frag[TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+        a_frag[i] = (wm * 32 * TM + i * 32 + l32) * kLdsRow + half * 16;
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+        b_frag[j] = (BM + wn * 32 * TN + j * 32 + l32) * kLdsRow + half * 16;
 
+    __syncthreads();
+    half8v af[2][TM], bf[2][TN];
+    if (nk > 0)
+        read_frags<TM, TN>(lds, a_frag, b_frag, 0, af[0], bf[0]);
     for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
+        const uint8_t *cur = lds + (kt & 1) * kStage;
+        const uint8_t *nxt = lds + ((kt + 1) & 1) * kStage;
         const bool more = kt + 1 < nk;
-        if (more) {
-            load_stage<BM>(ra, g.a_codes, g.a_scales, g.a2d, m0, g.M, g.K, kt + 1, kfull);
-            load_stage<BN>(rb, g.b_codes, g.b_scales, g.b2d, n0, g.N, g.K, kt + 1, kfull);
-        }
-        // fragments of this step: 16 code bytes (32 k values) + 2 scales per tile
-        uint4 ca[TM], cb[TN];
-        half2v sa[TM], sbv[TN];
-#pragma unroll
-        for (int i = 0; i < TM; i++) {
-            const int row = wm * 32 * TM + i * 32 + l32;
-            ca[i] = *reinterpret_cast<const uint4 *>(&lds_a[cur][row * kLdsStride + half * 16]);
-            const uint32_t sw = lds_as[cur][row] >> (16 * half);
-            sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int row = wn * 32 * TN + j * 32 + l32;
-            cb[j] = *reinterpret_cast<const uint4 *>(&lds_b[cur][row * kLdsStride + half * 16]);
-            const uint32_t sw = lds_bs[cur][row] >> (16 * half);
-            sbv[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-        }
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            half8v af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; i++) {
-                const uint32_t w = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
-                af[i] = dequant8(w, sa[i][s >> 1]);
+            const int p = s & 1;
+            if (s < 3)
+                read_frags<TM, TN>(cur, a_frag, b_frag, s + 1, af[p ^ 1], bf[p ^ 1]);
+            if (s == 3) {
+                // every fragment of stage kt is in registers: hand the buffer
+                // back, wait for stage kt+1, fetch its first fragments under
+                // this substep's MFMAs
+                __syncthreads();
+                if (more)
+                    read_frags<TM, TN>(nxt, a_frag, b_frag, 0, af[0], bf[0]);
             }
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const uint32_t w = s == 0 ? cb[j].x : s == 1 ? cb[j].y : s == 2 ? cb[j].z : cb[j].w;
-                bf[j] = dequant8(w, sbv[j][s >> 1]);
-            }
+            // weight fragment first: each lane's accumulator quad is then 4
+            // consecutive output columns (vector stores in the epilogue)
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[p][j], af[p][i], acc[i][j], 0, 0, 0);
+            if (s < 3) {
+                // spread the next substep's LDS reads between the MFMAs
+#pragma unroll
+                for (int h = 0; h < TM + TN; h++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
+            }
         }
-        if (more) {
-            store_stage<BM>(ra, lds_a[cur ^ 1], lds_as[cur ^ 1]);
-            store_stage<BN>(rb, lds_b[cur ^ 1], lds_bs[cur ^ 1]);
-        }
-        __syncthreads();
     }
 
-    // epilogue: 32x32 accumulator layout -- register r of lane l holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    // epilogue: register r of lane l holds C[row = l%32][col = 8*(r/4) +
+    // 4*(l/32) + r%4] of each 32x32 tile
     const float scale = *g.a_alpha * *g.b_alpha;
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+    for (int i = 0; i < TM; i++) {
+        const int row = m0 + wm * 32 * TM + i * 32 + l32;
+        if (row >= g.M)
+            continue;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int col = n0 + wn * 32 * TN + j * 32 + l32;
-            if (col >= g.N)
-                continue;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = m0 + wm * 32 * TM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (row < g.M) {
-                    const float v = acc[i][j][r] * scale;
+            for (int q = 0; q < 4; q++) {
+                const int col = n0 + wn * 32 * TN + j * 32 + 8 * q + 4 * half;
+                const float v0 = acc[i][j][4 * q + 0] * scale, v1 = acc[i][j][4 * q + 1] * scale;
+                const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
+                const int64_t off = (int64_t)row * g.ldc + col;
+                if (col + 3 < g.N && g.vec_ok) {
                     if (g.c_bf16) {
-                        __bf16 h = (__bf16)v;
-                        reinterpret_cast<uint16_t *>(g.c)[(int64_t)row * g.ldc + col] =
-                            __builtin_bit_cast(uint16_t, h);
+                        const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1, h2 = (__bf16)v2, h3 = (__bf16)v3;
+                        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                        const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(g.c) + off) = make_uint2(w0, w1);
                     } else {
-                        reinterpret_cast<float *>(g.c)[(int64_t)row * g.ldc + col] = v;
+                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.c) + off) =
+                            make_float4(v0, v1, v2, v3);
+                    }
+                } else {
+                    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        if (col + e < g.N) {
+                            if (g.c_bf16) {
+                                const __bf16 h = (__bf16)v[e];
+                                reinterpret_cast<uint16_t *>(g.c)[off + e] = __builtin_bit_cast(uint16_t, h);
+                            } else {
+                                reinterpret_cast<float *>(g.c)[off + e] = v[e];
+                            }
+                        }
                     }
                 }
             }
         }
+    }
 }
 
 template <int TM, int TN>
 static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
 {
-    const int tiles_m = (g.M + 64 * TM - 1) / (64 * TM);
+    g.tiles_m = (g.M + 64 * TM - 1) / (64 * TM);
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
-    const int64_t grid = (int64_t)tiles_m * g.tiles_n;
-    k_gemm_nvfp4<TM, TN><<<(unsigned)grid, 256, 0, s>>>(g);
+    const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
+    if (g.K % kBK == 0)
+        k_gemm_nvfp4<TM, TN, true><<<(unsigned)grid, 512, 0, s>>>(g);
+    else
+        k_gemm_nvfp4<TM, TN, false><<<(unsigned)grid, 512, 0, s>>>(g);
     return hipGetLastError();
+}
+
+// Estimated time of a tile shape: rounds of workgroups over the 256 CUs times
+// the per-tile work, inflated for smaller tiles (more LDS traffic and decode
+// per MFMA).
+static double tile_cost(int64_t m, int64_t n, int tm, int tn)
+{
+    const int64_t tiles = ((m + 64 * tm - 1) / (64 * tm)) * ((n + 64 * tn - 1) / (64 * tn));
+    const int64_t rounds = (tiles + 255) / 256;
+    const double work = (double)(64 * tm) * (64 * tn);
+    const double overhead = 1.0 + 0.5 * (1.0 / tm + 1.0 / tn);
+    return (double)rounds * work * overhead;
 }
 
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
@@ -273,16 +375,26 @@ hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, in
     g.b_codes = b.codes; g.b_scales = b.scales; g.b_alpha = b.alpha; g.b2d = b.scale2d;
     g.c = c; g.ldc = ldc; g.c_bf16 = cdtype == 1;
     g.M = (int)m; g.N = (int)n; g.K = (int)k;
-    g.tiles_n = 0;
-    // tile choice: the largest tile that still gives about one full round of
-    // workgroups over the 256 compute units
-    const int64_t t44 = ((m + 255) / 256) * ((n + 255) / 256);
-    const int64_t t24 = ((m + 127) / 128) * ((n + 255) / 256);
-    if (t44 >= 256)
-        return launch_tm_tn<4, 4>(g, s);
-    if (t24 >= 256)
-        return launch_tm_tn<2, 4>(g, s);
-    return launch_tm_tn<2, 2>(g, s);
+    g.tiles_m = g.tiles_n = 0;
+    const uintptr_t esz = cdtype == 1 ? 2 : 4;
+    g.vec_ok = ((uintptr_t)c % (4 * esz) == 0) && (ldc % 4 == 0);
+    // candidate tiles (TM, TN); 256x256 needs more registers than a 2-wave/SIMD launch has
+    const int cand[4][2] = {{3, 4}, {4, 3}, {2, 4}, {2, 2}};
+    int pick = 0;
+    double best = tile_cost(m, n, cand[0][0], cand[0][1]);
+    for (int i = 1; i < 4; i++) {
+        const double cst = tile_cost(m, n, cand[i][0], cand[i][1]);
+        if (cst < best) {
+            best = cst;
+            pick = i;
+        }
+    }
+    switch (pick) {
+    case 0: return launch_tm_tn<3, 4>(g, s);
+    case 1: return launch_tm_tn<4, 3>(g, s);
+    case 2: return launch_tm_tn<2, 4>(g, s);
+    default: return launch_tm_tn<2, 2>(g, s);
+    }
 }
 
 }  // namespace nvfp4
