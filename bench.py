@@ -47,10 +47,15 @@ def dev_bf16(bits):
 
 def time_events(fn, iters: int, warmup: int = 3) -> float:
     """Average milliseconds per call of fn() measured with events on the
-    current stream (where the library enqueues)."""
+    current stream (where the library enqueues), after >= 0.5 s of warm-up."""
     import torch
-    for _ in range(warmup):
-        fn(0)
+    t_end = time.perf_counter() + 0.5
+    i = 0
+    while time.perf_counter() < t_end or i < warmup:
+        fn(i)
+        i += 1
+        if i % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -83,8 +88,14 @@ def bench_linear(nv, sets, steps, warmup):
         x, w, y, ws = sets[i % len(sets)]
         nv.linear(x, w, torch.bfloat16, out=y, workspace=ws)
 
-    for i in range(warmup):
+    # clocks ramp up over the first few hundred milliseconds of sustained work
+    t_end = time.perf_counter() + 1.0
+    i = 0
+    while time.perf_counter() < t_end or i < warmup:
         step(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
