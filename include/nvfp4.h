@@ -28,7 +28,8 @@
  *             gives +-0 codes
  *   xhat    = (q * s) * alpha                    (two fp32 multiplies)
  *   error_c = per block row, fma chain e = fma(d, d, e) over the row's 16
- *             elements in index order, d = x - xhat; rows added in order;
+ *             elements in index order, d = fma(-(q * s), alpha, x) (the
+ *             exact residual, rounded once); rows added in order;
  *             4 is chosen only if error_4 < error_6.
  *
  * Layouts (row-major, element 2j in the LOW nibble of byte j, scales are

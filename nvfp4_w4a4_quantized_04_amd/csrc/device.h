@@ -69,17 +69,13 @@ __device__ __forceinline__ float e4m3_get(uint32_t w)
     return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
 }
 
-// One candidate encoding of a 16-element block row with block scale s:
-// codes of x * (1 / (s * alpha)) and the fma chain of squared errors of the
-// dequantized values (q * s) * alpha, continued from e.
-__device__ __forceinline__ void encode16(const float (&x)[16], float s, float alpha, uint32_t &c0,
+// One candidate encoding of a 16-element block row with block scale s and
+// kappa = 1 / (s * alpha) (0 when s == 0): codes of x * kappa, and the fma
+// chain of squared residuals d = x - q*s*alpha (exact product, one rounding),
+// continued from e.
+__device__ __forceinline__ void encode16(const float (&x)[16], float s, float kappa, float alpha, uint32_t &c0,
                                          uint32_t &c1, float &e)
 {
-    float kappa = 0.0f;
-    if (s != 0.0f) {
-        float d = s * alpha;
-        kappa = 1.0f / d;                 // IEEE division (correctly rounded)
-    }
     uint32_t w0 = 0, w1 = 0;
     w0 = e2m1_put2<0>(w0, x[0] * kappa, x[1] * kappa);
     w0 = e2m1_put2<1>(w0, x[2] * kappa, x[3] * kappa);
@@ -89,53 +85,74 @@ __device__ __forceinline__ void encode16(const float (&x)[16], float s, float al
     w1 = e2m1_put2<1>(w1, x[10] * kappa, x[11] * kappa);
     w1 = e2m1_put2<2>(w1, x[12] * kappa, x[13] * kappa);
     w1 = e2m1_put2<3>(w1, x[14] * kappa, x[15] * kappa);
-    float q[16];
-    float2v t;
-    t = e2m1_get2<0>(w0); q[0] = t[0]; q[1] = t[1];
-    t = e2m1_get2<1>(w0); q[2] = t[0]; q[3] = t[1];
-    t = e2m1_get2<2>(w0); q[4] = t[0]; q[5] = t[1];
-    t = e2m1_get2<3>(w0); q[6] = t[0]; q[7] = t[1];
-    t = e2m1_get2<0>(w1); q[8] = t[0]; q[9] = t[1];
-    t = e2m1_get2<1>(w1); q[10] = t[0]; q[11] = t[1];
-    t = e2m1_get2<2>(w1); q[12] = t[0]; q[13] = t[1];
-    t = e2m1_get2<3>(w1); q[14] = t[0]; q[15] = t[1];
+    // residual d = x - (q*s)*alpha with q*s formed exactly in fp16 (<= 6
+    // significant bits, within fp16's normal range) and a mixed-precision fma
+    // (exact operand conversion, one rounding): equal to fmaf(-(q*s), alpha, x)
+    const _Float16 sh = (_Float16)s;                 // E4M3 values are exact in fp16
+    const half2v ss = {sh, sh};
+    half2v qs[8];
+    qs[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0) * ss;
+    qs[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1) * ss;
+    qs[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) * ss;
+    qs[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) * ss;
+    qs[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0) * ss;
+    qs[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1) * ss;
+    qs[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) * ss;
+    qs[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) * ss;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        float xh = (q[i] * s) * alpha;
-        float d = x[i] - xh;
+        const float d = __builtin_fmaf(-(float)qs[i >> 1][i & 1], alpha, x[i]);
         e = __builtin_fmaf(d, d, e);
     }
     c0 = w0;
     c1 = w1;
 }
 
-// Quantize one 1D block of 16 values (RULE4: four-over-six).  Returns the
-// codes (8 bytes) and the E4M3 scale byte.
+// kappa = RN(1 / RN(s * alpha)) for every E4M3 scale byte b in [0, 128), 0 for
+// s == 0; built once per workgroup so blocks look it up instead of dividing.
+// Every thread of the workgroup must call it (it synchronizes).
+__device__ __forceinline__ void build_kappa_table(float *tab, float alpha)
+{
+    for (int b = threadIdx.x; b < 128; b += blockDim.x) {
+        const float s = __builtin_amdgcn_cvt_f32_fp8(b, 0);
+        float k = 0.0f;
+        if (b != 0 && b < 127) {            // byte 127 (NaN) never occurs: scales are clamped to 448
+            const float d = s * alpha;
+            k = 1.0f / d;                   // IEEE division (correctly rounded)
+        }
+        tab[b] = k;
+    }
+    __syncthreads();
+}
+
+// Quantize one 1D block of 16 values (RULE4: four-over-six): codes (8 bytes)
+// and the E4M3 scale byte.  ktab: the workgroup's kappa table.
 template <bool RULE4>
-__device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha, uint32_t &c0,
+__device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha, const float *ktab, uint32_t &c0,
                                               uint32_t &c1, uint32_t &sbyte)
 {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i++)
         m = fmaxf(m, fabsf(x[i]));
-    float mu = m / alpha;
-    float t6 = mu / 6.0f;
-    float t4 = mu * 0.25f;                 // == RN(mu / 4)
-    uint32_t sb = e4m3_put2(t6, t4);       // byte0: s6, byte1: s4
-    float s6 = e4m3_get<0>(sb);
+    const float mu = m / alpha;
+    const float t6 = mu / 6.0f;
+    const float t4 = mu * 0.25f;                 // == RN(mu / 4)
+    const uint32_t sb = e4m3_put2(t6, t4);       // byte0: s6, byte1: s4
+    const uint32_t b6 = sb & 0xffu, b4 = (sb >> 8) & 0xffu;
+    const float s6 = e4m3_get<0>(sb);
     float e6 = 0.0f;
-    encode16(x, s6, alpha, c0, c1, e6);
-    sbyte = sb & 0xffu;
+    encode16(x, s6, ktab[b6], alpha, c0, c1, e6);
+    sbyte = b6;
     if (RULE4) {
-        float s4 = e4m3_get<1>(sb);
+        const float s4 = e4m3_get<1>(sb);
         uint32_t d0, d1;
         float e4 = 0.0f;
-        encode16(x, s4, alpha, d0, d1, e4);
+        encode16(x, s4, ktab[b4], alpha, d0, d1, e4);
         if (e4 < e6) {
             c0 = d0;
             c1 = d1;
-            sbyte = (sb >> 8) & 0xffu;
+            sbyte = b4;
         }
     }
 }

@@ -39,56 +39,51 @@ __device__ __forceinline__ float block_alpha(const float *__restrict__ amax_src,
 // ---------------------------------------------------------------- amax
 
 template <typename T>
-__global__ __launch_bounds__(kQuantThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
-                                                        int64_t ldx, float *__restrict__ partials)
+__device__ __forceinline__ float absmax16B(uint4 v, float a)
 {
-    __shared__ float red[kQuantThreads / 64];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (sizeof(T) == 2)
+            a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+        else
+            a = fmaxf(a, fabsf(__uint_as_float(w[j])));
+    }
+    return a;
+}
+
+// Partial maxima: kAmaxThreads threads per workgroup, each keeping
+// kAmaxUnroll 16-byte loads in flight per iteration.
+template <typename T>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                       int64_t ldx, float *__restrict__ partials)
+{
+    __shared__ float red[kAmaxThreads / 64];
     float a = 0.0f;
     if (ldx == cols) {
-        // contiguous: 16-byte vectors, grid-stride
         constexpr int V = 16 / sizeof(T);
         const int64_t n = rows * cols;
         const int64_t nv = n / V;
-        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-        int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-        for (; i + 3 * stride < nv; i += 4 * stride) {
-            uint4 v[4];
+        const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+        const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+        int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+        for (; i + (kAmaxUnroll - 1) * stride < nv; i += kAmaxUnroll * stride) {
+            uint4 v[kAmaxUnroll];
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                v[u] = reinterpret_cast<const uint4 *>(x)[i + u * stride];
+            for (int u = 0; u < kAmaxUnroll; u++)
+                v[u] = xv[i + u * stride];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    if (sizeof(T) == 2) {
-                        a = fmaxf(a, fabsf(bf16_lo(w[j])));
-                        a = fmaxf(a, fabsf(bf16_hi(w[j])));
-                    } else {
-                        a = fmaxf(a, fabsf(__uint_as_float(w[j])));
-                    }
-                }
-            }
+            for (int u = 0; u < kAmaxUnroll; u++)
+                a = absmax16B<T>(v[u], a);
         }
-        for (; i < nv; i += stride) {
-            uint4 v = reinterpret_cast<const uint4 *>(x)[i];
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if (sizeof(T) == 2) {
-                    a = fmaxf(a, fabsf(bf16_lo(w[j])));
-                    a = fmaxf(a, fabsf(bf16_hi(w[j])));
-                } else {
-                    a = fmaxf(a, fabsf(__uint_as_float(w[j])));
-                }
-            }
-        }
-        for (int64_t t = nv * V + (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; t < n; t += stride)
+        for (; i < nv; i += stride)
+            a = absmax16B<T>(xv[i], a);
+        for (int64_t t = nv * V + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < n; t += stride)
             a = fmaxf(a, fabsf(load1(x + t)));
     } else {
-        // strided rows: one row per block iteration, threads along the row
+        // strided rows: rows spread over workgroups, threads along the row
         for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
-            for (int64_t c = threadIdx.x; c < cols; c += kQuantThreads)
+            for (int64_t c = threadIdx.x; c < cols; c += kAmaxThreads)
                 a = fmaxf(a, fabsf(load1(x + r * ldx + c)));
     }
     a = wave_max(a);
@@ -98,7 +93,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_amax(const T *__restrict__ x,
     if (threadIdx.x == 0) {
         float b = red[0];
 #pragma unroll
-        for (int w = 1; w < kQuantThreads / 64; w++)
+        for (int w = 1; w < kAmaxThreads / 64; w++)
             b = fmaxf(b, red[w]);
         partials[blockIdx.x] = b;
     }
@@ -106,8 +101,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_amax(const T *__restrict__ x,
 
 // ------------------------------------------------------ ROW16 (1D, along cols)
 
-// One lane per 16-element block; blocks numbered row-major, so the codes of
-// block b are bytes [8b, 8b+8) and its scale is byte b (cols % 16 == 0).
+// Each lane quantizes kRowBlocks whole 16-element blocks held in its own
+// registers (blocks b, b+256, ... of the workgroup's range, so every load and
+// store instruction of a wave is contiguous).  Blocks are numbered row-major:
+// block b's codes are bytes [8b, 8b+8), its scale is byte b (cols % 16 == 0).
 template <typename T, bool RULE4>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restrict__ x, int64_t rows, int64_t bpr,
                                                                int64_t ldx, const float *__restrict__ amax_src,
@@ -115,20 +112,41 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
                                                                uint8_t *__restrict__ scales,
                                                                float *__restrict__ alpha_out)
 {
+    __shared__ float ktab[128];
+    const int64_t nb = rows * bpr;
+    const bool flat = ldx == bpr * 16;
+    const int64_t b0 = (int64_t)blockIdx.x * (kQuantThreads * kRowBlocks) + threadIdx.x;
+    // issue the data loads first; alpha and the kappa table are set up while
+    // they are in flight
+    float v[kRowBlocks][16];
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; j++) {
+        const int64_t b = b0 + j * kQuantThreads;
+        if (b < nb) {
+            int64_t off;
+            if (flat) {
+                off = b * 16;
+            } else {
+                const int64_t r = b / bpr;
+                off = r * ldx + (b - r * bpr) * 16;
+            }
+            load16(x + off, v[j]);
+        }
+    }
     const float alpha = block_alpha(amax_src, n_amax);
+    build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
-    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-    if (b >= rows * bpr)
-        return;
-    const int64_t r = b / bpr;
-    const int64_t cb = b - r * bpr;
-    float v[16];
-    load16(x + r * ldx + cb * 16, v);
-    uint32_t c0, c1, sb;
-    quant_block16<RULE4>(v, alpha, c0, c1, sb);
-    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
-    scales[b] = (uint8_t)sb;
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; j++) {
+        const int64_t b = b0 + j * kQuantThreads;
+        if (b < nb) {
+            uint32_t c0, c1, sb;
+            quant_block16<RULE4>(v[j], alpha, ktab, c0, c1, sb);
+            *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
+            scales[b] = (uint8_t)sb;
+        }
+    }
 }
 
 // ------------------------------------------------ COL16 (1D, along rows)
@@ -144,7 +162,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
                                                                uint8_t *__restrict__ scales,
                                                                float *__restrict__ alpha_out)
 {
+    __shared__ float ktab[128];
     const float alpha = block_alpha(amax_src, n_amax);
+    build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
     const int64_t c = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
@@ -162,7 +182,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
             for (int i = 0; i < 16; i++)
                 v[i] = load1(p + i * ldx);
             uint32_t c0, c1, sb;
-            quant_block16<RULE4>(v, alpha, c0, c1, sb);
+            quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
             *reinterpret_cast<uint2 *>(codes + c * (rows / 2) + rb * 8) = make_uint2(c0, c1);
             scales[c * nrb + rb] = (uint8_t)sb;
         }
@@ -180,7 +200,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restr
                                                                 uint8_t *__restrict__ scales,
                                                                 float *__restrict__ alpha_out)
 {
+    __shared__ float ktab[128];
     const float alpha = block_alpha(amax_src, n_amax);
+    build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
     const int lane16 = threadIdx.x & 15;
@@ -206,7 +228,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restr
         const float s6 = e4m3_get<0>(sb);
         uint32_t c0, c1;
         float er = 0.0f;
-        encode16(v, s6, alpha, c0, c1, er);
+        encode16(v, s6, ktab[sb & 0xffu], alpha, c0, c1, er);
         float e6 = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i++)
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restr
             const float s4 = e4m3_get<1>(sb);
             uint32_t d0, d1;
             float er4 = 0.0f;
-            encode16(v, s4, alpha, d0, d1, er4);
+            encode16(v, s4, ktab[(sb >> 8) & 0xffu], alpha, d0, d1, er4);
             float e4 = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; i++)
@@ -325,7 +347,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_col16(const uint8_t *
 int amax_partials(int64_t rows, int64_t cols)
 {
     const int64_t n = rows * cols;
-    int64_t p = (n + (int64_t)kQuantThreads * 64 - 1) / ((int64_t)kQuantThreads * 64);
+    const int64_t per_wg = (int64_t)kAmaxThreads * kAmaxUnroll * 8 * 4;   // ~4 iterations of 8-element loads
+    int64_t p = (n + per_wg - 1) / per_wg;
     if (p < 1) p = 1;
     if (p > kMaxAmaxPartials) p = kMaxAmaxPartials;
     return (int)p;
@@ -335,9 +358,9 @@ hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int
                        int n_partials, hipStream_t s)
 {
     if (dtype == 1)
-        k_amax<uint16_t><<<n_partials, kQuantThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, partials);
+        k_amax<uint16_t><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, partials);
     else
-        k_amax<float><<<n_partials, kQuantThreads, 0, s>>>((const float *)x, rows, cols, ldx, partials);
+        k_amax<float><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, partials);
     return hipGetLastError();
 }
 
@@ -348,7 +371,8 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
     if (block == 0) {
         const int64_t bpr = cols / 16;
         const int64_t nb = rows * bpr;
-        const unsigned grid = (unsigned)((nb + kQuantThreads - 1) / kQuantThreads);
+        const int64_t per_wg = (int64_t)kQuantThreads * kRowBlocks;
+        const unsigned grid = (unsigned)((nb + per_wg - 1) / per_wg);
         k_quant_row16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
     } else if (block == 1) {
         const int64_t tpr = cols / 16;

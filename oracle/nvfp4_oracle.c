@@ -30,10 +30,11 @@
  *   R3  fp32 evaluation order: mu = RN32(m / alpha); t_c = RN32(mu / c);
  *       s_c = E4M3(t_c); d_c = RN32(s_c * alpha); kappa_c = RN32(1 / d_c)
  *       (0 when s_c == 0); v = RN32(x * kappa_c); code = E2M1(v).
- *   R4  candidate error in the X domain against the library's own fp32
- *       dequantization xhat = RN32(RN32(q * s) * alpha): per block row an
- *       fmaf chain e = fma(d, d, e) over the row's 16 elements in index order
- *       (d = RN32(x - xhat)), rows summed in order; choose 4 iff e4 < e6.
+ *   R4  candidate error in the X domain: the residual d = x - q*s*alpha of
+ *       each element with the exact product and a single rounding
+ *       (d = fmaf(-(q*s), alpha, x); q*s is exact), then per block row an
+ *       fmaf chain e = fma(d, d, e) over the row's 16 elements in index
+ *       order, rows summed in order; choose 4 iff e4 < e6.
  *   R5  E4M3 rounding: nearest finite E4FN value, ties to even, subnormals
  *       kept, saturating at 448 (never NaN).
  *   R6  E2M1 rounding: nearest, ties to even, saturating at 6, the sign bit
@@ -214,8 +215,7 @@ static void encode_candidate(const float *xs, int n, float mu, float alpha, floa
             int code = nvo_e2m1_encode(v);
             float q = (float)nvo_e2m1_value(code);
             float qs = q * s;                   /* exact: <= 6 significant bits */
-            float xh = qs * alpha;
-            float d = x - xh;
+            float d = fmaf(-qs, alpha, x);      /* x - q*s*alpha, exact product, one rounding */
             er = fmaf(d, d, er);
             out->codes[r * 16 + j] = code;
         }
