@@ -97,7 +97,7 @@ int nvfp4_abi_version(void);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* Bytes of workspace nvfp4_quantize / nvfp4_kv_quantize need (amax partial
- * maxima).  Never more than 4 KiB. */
+ * maxima).  Never more than 4 KiB (currently 1 KiB). */
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 
 /*
@@ -141,6 +141,10 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, con
  *   tensor of x [k][r] is the operand x^T [r][k] with 1D scales.
  *   k % 16 == 0; 2D scales need the operand's row count % 16 == 0.
  *   C [m][n], row stride ldc, dtype NVFP4_F32 or NVFP4_BF16.
+ *   c_amax (optional, device, 4-byte aligned): receives max |C| over the
+ *   stored values (after bf16 rounding for bf16 output) -- the amax a
+ *   following nvfp4_quantize / nvfp4_kv_quantize of C needs, so that call
+ *   can skip its own amax pass.  NULL: not computed.
  * The dequantized operands q*s are exact in fp16, so the contraction runs on
  * fp16 MFMA with fp32 accumulation; accumulation order is unspecified.
  * Source: "The three GEMMs of backpropagation" and "Quantization-
@@ -151,7 +155,7 @@ nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
                           const uint8_t *b_codes, const uint8_t *b_scales, const float *b_alpha,
                           int b_scale_layout,
                           int64_t m, int64_t n, int64_t k,
-                          void *c, int c_dtype, int64_t ldc, hipStream_t stream);
+                          void *c, int c_dtype, int64_t ldc, float *c_amax, hipStream_t stream);
 
 /*
  * nvfp4_kv_quantize -- quantize one K or V cache tensor of `vectors` rows of
@@ -159,12 +163,14 @@ nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
  * [tokens][heads], contiguous, so vectors = heads * tokens), 16-element
  * blocks along head_dim, one alpha for the whole tensor.  Equivalent to
  * nvfp4_quantize(kv, dtype, vectors, head_dim, head_dim, NVFP4_ROW16, rule,
- * NULL, ...).  head_dim % 16 == 0.
+ * amax, ...).  head_dim % 16 == 0.  amax: NULL (computed, one extra read of
+ * the tensor) or a device pointer to the tensor's max |x|, e.g. the c_amax
+ * output of the GEMM that produced K or V (single pass over the tensor).
  * Source: "KV cache quantization" / "Chunkwise quantization procedure"
  * (NVFP4 Inference section of the architecture walkthrough page).
  */
 nvfp4_status_t nvfp4_kv_quantize(const void *kv, int kv_dtype, int64_t vectors, int64_t head_dim,
-                                 int rule, uint8_t *codes, uint8_t *scales, float *alpha,
+                                 int rule, const float *amax, uint8_t *codes, uint8_t *scales, float *alpha,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace of nvfp4_linear: the packed activation (m*k*9/16 bytes) plus the
@@ -176,13 +182,14 @@ size_t nvfp4_linear_workspace_size(int64_t m, int64_t k);
  * into the call: quantize x [m][k] (ROW16, `rule`, amax computed on the
  * device) into the workspace, then y = nvfp4_gemm(x_packed, w).
  *   w: packed weight [n][k] (TILE16 -> NVFP4_SCALE_2D, ROW16 -> _1D).
+ *   y_amax: optional max |y| output, as c_amax of nvfp4_gemm.
  * Source: "Quantization-dequantization flow" (FPROP: weight x activation ->
  * BF16 output).
  */
 nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                             int w_scale_layout, int64_t n,
-                            void *y, int y_dtype, int64_t ldy,
+                            void *y, int y_dtype, int64_t ldy, float *y_amax,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace of nvfp4_wgrad: both COL16-packed operands plus amax partials. */

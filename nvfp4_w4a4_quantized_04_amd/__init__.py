@@ -54,13 +54,13 @@ def _load():
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i32, P, i32, i64, P]
     L.nvfp4_gemm.restype = i32
-    L.nvfp4_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, P, i32, i64, P]
+    L.nvfp4_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, P, i32, i64, P, P]
     L.nvfp4_kv_quantize.restype = i32
-    L.nvfp4_kv_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, P, sz, P]
+    L.nvfp4_kv_quantize.argtypes = [P, i32, i64, i64, i32, P, P, P, P, P, sz, P]
     L.nvfp4_linear_workspace_size.restype = sz
     L.nvfp4_linear_workspace_size.argtypes = [i64, i64]
     L.nvfp4_linear.restype = i32
-    L.nvfp4_linear.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, sz, P]
+    L.nvfp4_linear.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, P, sz, P]
     L.nvfp4_wgrad_workspace_size.restype = sz
     L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_wgrad.restype = i32
@@ -185,8 +185,10 @@ def dequantize(t: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = N
     return out
 
 
-def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
-    """C = alpha_A alpha_B Ahat Bhat^T on packed operands."""
+def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None,
+         amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = alpha_A alpha_B Ahat Bhat^T on packed operands.  amax_out (float32
+    [1], optional) receives max |C| of the stored values."""
     ca, sa, aa, la, m, k = a.operand()
     cb, sb, ab, lb, n, kb = b.operand()
     if k != kb:
@@ -196,13 +198,14 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Ten
         out = torch.empty((m, n), dtype=out_dtype, device=ca.device)
     _check("nvfp4_gemm", lib.nvfp4_gemm(
         _ptr(ca), _ptr(sa), _ptr(aa), la, _ptr(cb), _ptr(sb), _ptr(ab), lb, m, n, k,
-        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _stream()))
     return out
 
 
 def kv_quantize(kv: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
-                workspace: torch.Tensor | None = None) -> NVFP4Tensor:
-    """Quantize a K or V cache tensor [..., head_dim] (``quantize_kv``)."""
+                workspace: torch.Tensor | None = None, amax: torch.Tensor | None = None) -> NVFP4Tensor:
+    """Quantize a K or V cache tensor [..., head_dim] (``quantize_kv``).  amax:
+    optional device float32 [1] holding max |kv| (single pass)."""
     _need_gpu(kv)
     if not kv.is_contiguous():
         raise ValueError("kv must be contiguous")
@@ -213,8 +216,8 @@ def kv_quantize(kv: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(vectors, d), dtype=torch.uint8, device=kv.device)
     _check("nvfp4_kv_quantize", lib.nvfp4_kv_quantize(
-        _ptr(kv), _dtype_code(kv), vectors, d, _rule(rule), _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha),
-        _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(kv), _dtype_code(kv), vectors, d, _rule(rule), _ptr(amax), _ptr(out.codes), _ptr(out.scales),
+        _ptr(out.alpha), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
@@ -223,8 +226,10 @@ def linear_workspace(m: int, k: int, device="cuda") -> torch.Tensor:
 
 
 def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4over6",
-           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A4 forward: y = quantize(x) @ w^T with the activation quantizer fused in the call."""
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A4 forward: y = quantize(x) @ w^T with the activation quantizer fused in
+    the call.  amax_out (float32 [1], optional) receives max |y|."""
     _need_gpu(x)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2D with unit column stride")
@@ -238,7 +243,8 @@ def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4ove
         workspace = linear_workspace(m, k, x.device)
     _check("nvfp4_linear", lib.nvfp4_linear(
         _ptr(x), _dtype_code(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n,
-        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _ptr(workspace), workspace.numel(),
+        _stream()))
     return out
 
 

@@ -139,7 +139,8 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, con
 
 nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_alpha, int a_scale_layout,
                           const uint8_t *b_codes, const uint8_t *b_scales, const float *b_alpha, int b_scale_layout,
-                          int64_t m, int64_t n, int64_t k, void *c, int c_dtype, int64_t ldc, hipStream_t stream)
+                          int64_t m, int64_t n, int64_t k, void *c, int c_dtype, int64_t ldc, float *c_amax,
+                          hipStream_t stream)
 {
     if (!dtype_ok(c_dtype))
         return NVFP4_ERR_DTYPE;
@@ -158,20 +159,20 @@ nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
     }
     if ((c && !aligned_elem(c, c_dtype)) || (a_codes && !aligned16(a_codes)) ||
         (b_codes && !aligned16(b_codes)) || (a_scales && !aligned16(a_scales)) ||
-        (b_scales && !aligned16(b_scales)))
+        (b_scales && !aligned16(b_scales)) || (c_amax && ((uintptr_t)c_amax & 3u) != 0))
         return NVFP4_ERR_ALIGN;
     GemmOperand A{a_codes, a_scales, a_alpha, a_scale_layout};
     GemmOperand B{b_codes, b_scales, b_alpha, b_scale_layout};
-    return launch_status(launch_gemm(A, B, m, n, k, c, c_dtype, ldc, stream));
+    return launch_status(launch_gemm(A, B, m, n, k, c, c_dtype, ldc, c_amax, stream));
 }
 
 nvfp4_status_t nvfp4_kv_quantize(const void *kv, int kv_dtype, int64_t vectors, int64_t head_dim, int rule,
-                                 uint8_t *codes, uint8_t *scales, float *alpha, void *workspace,
-                                 size_t workspace_bytes, hipStream_t stream)
+                                 const float *amax, uint8_t *codes, uint8_t *scales, float *alpha,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (head_dim % 16 != 0)
         return NVFP4_ERR_SHAPE;
-    return nvfp4_quantize(kv, kv_dtype, vectors, head_dim, head_dim, NVFP4_ROW16, rule, nullptr, codes, scales,
+    return nvfp4_quantize(kv, kv_dtype, vectors, head_dim, head_dim, NVFP4_ROW16, rule, amax, codes, scales,
                           alpha, workspace, workspace_bytes, stream);
 }
 
@@ -186,8 +187,8 @@ size_t nvfp4_linear_workspace_size(int64_t m, int64_t k)
 
 nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
-                            int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, void *workspace,
-                            size_t workspace_bytes, hipStream_t stream)
+                            int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, float *y_amax,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype) || !rule_ok(rule) ||
         (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
@@ -198,6 +199,7 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
     if (!w_alpha || (m > 0 && n > 0 && !y) || (m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!w_codes || !w_scales)))
         return NVFP4_ERR_NULL;
     if (ldx % 8 != 0 || (x && !aligned16(x)) || (y && !aligned_elem(y, y_dtype)) ||
+        (y_amax && ((uintptr_t)y_amax & 3u) != 0) ||
         (w_codes && !aligned16(w_codes)) || (w_scales && !aligned16(w_scales)))
         return NVFP4_ERR_ALIGN;
     if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
@@ -215,7 +217,7 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
         return st;
     GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};
     GemmOperand B{w_codes, w_scales, w_alpha, w_scale_layout};
-    return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, stream));
+    return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, y_amax, stream));
 }
 
 // workspace: [alpha_dy][alpha_x] (256 B), [partials dy][partials x],
@@ -264,7 +266,7 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
         return st;
     GemmOperand A{c_dy, s_dy, alpha_dy, NVFP4_SCALE_1D};
     GemmOperand B{c_x, s_x, alpha_x, NVFP4_SCALE_1D};
-    return launch_status(launch_gemm(A, B, n_out, k_in, tokens, dw, dw_dtype, lddw, stream));
+    return launch_status(launch_gemm(A, B, n_out, k_in, tokens, dw, dw_dtype, lddw, nullptr, stream));
 }
 
 }  // extern "C"

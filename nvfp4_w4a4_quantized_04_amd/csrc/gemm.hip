@@ -44,6 +44,7 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int c_bf16;
     int vec_ok;     // C pointer and ldc allow 4-element vector stores
+    float *c_amax;  // optional: max |C| of the stored values (atomic max, zeroed before the launch)
 };
 
 template <int B, int E, typename F>
@@ -296,6 +297,7 @@ void k_gemm_nvfp4(GemmArgs g)
     // epilogue: register r of lane l holds C[row = l%32][col = 8*(r/4) +
     // 4*(l/32) + r%4] of each 32x32 tile
     const float scale = *g.a_alpha * *g.b_alpha;
+    float amax = 0.0f;                  // max |C| over this lane's stored outputs
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int row = m0 + wm * 32 * TM + i * 32 + l32;
@@ -309,6 +311,8 @@ void k_gemm_nvfp4(GemmArgs g)
                 const float v0 = acc[i][j][4 * q + 0] * scale, v1 = acc[i][j][4 * q + 1] * scale;
                 const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
                 const int64_t off = (int64_t)row * g.ldc + col;
+                if (col + 3 < g.N)
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
                 if (col + 3 < g.N && g.vec_ok) {
                     if (g.c_bf16) {
                         const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1, h2 = (__bf16)v2, h3 = (__bf16)v3;
@@ -326,6 +330,7 @@ void k_gemm_nvfp4(GemmArgs g)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         if (col + e < g.N) {
+                            amax = fmaxf(amax, fabsf(v[e]));
                             if (g.c_bf16) {
                                 const __bf16 h = (__bf16)v[e];
                                 reinterpret_cast<uint16_t *>(g.c)[off + e] = __builtin_bit_cast(uint16_t, h);
@@ -337,6 +342,15 @@ void k_gemm_nvfp4(GemmArgs g)
                 }
             }
         }
+    }
+    if (g.c_amax) {
+        // rounding to bf16 is monotone: the max of the stored values is the
+        // rounded max
+        if (g.c_bf16)
+            amax = (float)(__bf16)amax;
+        amax = wave_max(amax);
+        if (lane == 0)
+            atomicMax(reinterpret_cast<unsigned int *>(g.c_amax), __float_as_uint(amax));
     }
 }
 
@@ -365,12 +379,23 @@ static double tile_cost(int64_t m, int64_t n, int tm, int tn)
     return (double)rounds * work * overhead;
 }
 
+__global__ void k_zero_float(float *p) { *p = 0.0f; }
+
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
-                       int cdtype, int64_t ldc, hipStream_t s)
+                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s)
 {
+    if (c_amax) {
+        // non-negative floats order like their bit patterns: the epilogue
+        // combines workgroups with an unsigned atomic max on a zeroed word
+        k_zero_float<<<1, 1, 0, s>>>(c_amax);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     if (m == 0 || n == 0)
         return hipSuccess;
     GemmArgs g;
+    g.c_amax = c_amax;
     g.a_codes = a.codes; g.a_scales = a.scales; g.a_alpha = a.alpha; g.a2d = a.scale2d;
     g.b_codes = b.codes; g.b_scales = b.scales; g.b_alpha = b.alpha; g.b2d = b.scale2d;
     g.c = c; g.ldc = ldc; g.c_bf16 = cdtype == 1;

@@ -38,7 +38,8 @@ struct GemmOperand {
     int scale2d;
 };
 
+// c_amax (optional): receives max |C| of the stored values
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
-                       int cdtype, int64_t ldc, hipStream_t s);
+                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s);
 
 }  // namespace nvfp4

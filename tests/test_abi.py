@@ -69,25 +69,26 @@ def test_gemm_and_linear_validation_without_gpu():
     import nvfp4_w4a4_quantized_04_amd as m
     g = m.lib.nvfp4_gemm
     ok = (FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1)
-    assert g(*ok, 32, 32, 24, FAKE, 0, 32, None) == 2          # k % 16
-    assert g(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 32, 24, 32, FAKE, 0, 24, None) == 2  # 2D needs n % 16
-    assert g(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1, 32, 32, 32, FAKE, 0, 32, None) == 4
-    assert g(*ok, 32, 32, 32, FAKE, 3, 32, None) == 4
-    assert g(*ok, 32, 32, 32, None, 0, 32, None) == 1
-    assert g(*ok, 32, 32, 32, FAKE + 2, 0, 36, None) == 3       # fp32 C needs 4-byte alignment
+    assert g(*ok, 32, 32, 24, FAKE, 0, 32, None, None) == 2          # k % 16
+    assert g(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 32, 24, 32, FAKE, 0, 24, None, None) == 2  # 2D needs n % 16
+    assert g(FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1, 32, 32, 32, FAKE, 0, 32, None, None) == 4
+    assert g(*ok, 32, 32, 32, FAKE, 3, 32, None, None) == 4
+    assert g(*ok, 32, 32, 32, None, 0, 32, None, None) == 1
+    assert g(*ok, 32, 32, 32, FAKE + 2, 0, 36, None, None) == 3       # fp32 C needs 4-byte alignment
+    assert g(*ok, 32, 32, 32, FAKE, 0, 36, FAKE + 2, None) == 3        # amax output needs 4-byte alignment
     lin = m.lib.nvfp4_linear
-    assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, FAKE, 10, None) == 5
+    assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None, FAKE, 10, None) == 5
     need = m.lib.nvfp4_linear_workspace_size(32, 64)
     assert need >= 32 * 64 * 9 // 16
-    assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, FAKE + 16, need, None) == 3
+    assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None, FAKE + 16, need, None) == 3
     w = m.lib.nvfp4_wgrad
     assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
 
 
 def test_kv_quantize_validation_without_gpu():
     import nvfp4_w4a4_quantized_04_amd as m
-    assert m.lib.nvfp4_kv_quantize(FAKE, 1, 100, 120, 1, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2
-    assert m.lib.nvfp4_kv_quantize(FAKE, 1, 100, 128, 1, FAKE, FAKE, FAKE, None, 0, None) == 5
+    assert m.lib.nvfp4_kv_quantize(FAKE, 1, 100, 120, 1, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2
+    assert m.lib.nvfp4_kv_quantize(FAKE, 1, 100, 128, 1, None, FAKE, FAKE, FAKE, None, 0, None) == 5
 
 
 def test_no_cpu_fallback():

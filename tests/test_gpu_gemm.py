@@ -95,3 +95,35 @@ def test_wgrad_col16():
     B = oracle.quantize(x, oracle.COL16, 1)
     ref = oracle.gemm_f64(A, B)
     assert rel_frobenius(host_bits(dw), ref) <= GEMM_RTOL
+
+
+def test_epilogue_amax_output():
+    """c_amax / y_amax equal max |C| of the stored outputs (fp32 and bf16)."""
+    c = workloads.config2(m=300, k=512, n=384)
+    W = packed_to_device(oracle.quantize(c["w"], oracle.TILE16, 1))
+    xd = dev_from_host(c["x"])
+    for dt in (torch.float32, torch.bfloat16):
+        am = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")   # the call must overwrite it
+        y = nv.linear(xd, W, dt, amax_out=am)
+        torch.cuda.synchronize()
+        assert am.item() == y.float().abs().max().item()
+    A = packed_to_device(oracle.quantize(c["x"], oracle.ROW16, 1))
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y = nv.gemm(A, W, torch.float32, amax_out=am)
+    torch.cuda.synchronize()
+    assert am.item() == y.abs().max().item()
+
+
+def test_kv_projection_amax_feeds_single_pass_kv_quantize():
+    """K = linear(x, W_k) with the epilogue amax, then a single-pass KV
+    quantize: identical to the oracle's quantization of the stored K."""
+    c = workloads.config2(m=880, k=256, n=128 * 3)
+    W = packed_to_device(oracle.quantize(c["w"], oracle.TILE16, 1))
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    k = nv.linear(dev_from_host(c["x"]), W, torch.bfloat16, amax_out=am)
+    t1 = nv.kv_quantize(k.view(-1, 128), "4over6", amax=am)
+    t2 = nv.kv_quantize(k.view(-1, 128), "4over6")
+    torch.cuda.synchronize()
+    ref = oracle.quantize(host_bits(k).reshape(-1, 128), oracle.ROW16, 1)
+    assert_packed_equal(t1, ref, "single pass")
+    assert_packed_equal(t2, ref, "two pass")
