@@ -16,7 +16,9 @@ The same JSON line also carries
   cpu_baseline  the CPU oracle (fp32 quantizer, fp64 GEMM) on the full QKV
                 step on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--parts qkv,kv,extra,cpu]
+       python bench.py --copy-calibration   (a plain 256 MiB device copy, for
+                                             scaling rocprofv3 byte counters)
 """
 from __future__ import annotations
 
@@ -33,6 +35,22 @@ METRIC = "NVFP4 W4A4 GEMM TFLOPS incl. act-quantize at DiT shapes; KV-quantize G
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0       # dense fp16/bf16 MFMA, MI355X
 FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
+
+
+# HBM bytes per launch of the QKV-shaped GEMM kernel, from rocprofv3 byte
+# counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
+# counters read for a plain 256 MiB device copy.  They hold for the GEMM
+# source they were taken with only: null once gemm.hip has changed.
+GEMM_TRAFFIC = {"gemm_src_sha256": "4e45716f04ddb85772882a24dc970e5bc937a3d3701391b9f65a55efbf705fde",
+                "bytes_per_launch": 140371628}
+
+
+def gemm_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "nvfp4_w4a4_quantized_04_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    return GEMM_TRAFFIC["bytes_per_launch"] if h == GEMM_TRAFFIC["gemm_src_sha256"] else None
 
 
 def log(msg):
@@ -230,10 +248,29 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--parts", default="qkv,kv,extra,cpu",
+                    help="comma list of qkv (the step), kv, extra, cpu")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-kv", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    parts = set(args.parts.split(","))
+    if args.no_cpu:
+        parts.discard("cpu")
+    if args.no_extra:
+        parts.discard("extra")
+    if args.no_kv:
+        parts.discard("kv")
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the NVFP4 path here is built and timed on a single MI355X "
               "(multi-GPU sharding is a design note, not a measured run)", file=sys.stderr)
@@ -245,43 +282,44 @@ def main():
 
     assert torch.cuda.is_available()
     m, k, n = 2640, 3072, 9216
-    log("[bench] preparing QKV projection inputs")
-    sets = linear_sets(nv, workloads, m, k, n, 3, 2)
-    log("[bench] timing the fused linear")
-    ms = bench_linear(nv, sets, args.steps, args.warmup)
     flops = 2.0 * m * n * k
-    value = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] linear {ms:.4f} ms/step, {value:.1f} TFLOP/s")
-
-    log("[bench] timing the GEMM kernel alone")
-    gms = bench_gemm_kernel(nv, sets, max(50, args.steps // 2))
-    achieved = flops / (gms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "k_gemm_nvfp4", "kernel_ms": round(gms, 5),
-                "frac_of_fp4_mfma_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4)}
-    del sets
-    torch.cuda.empty_cache()
-
     result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "nvfp4 operands, f16 mfma (exact), f32 accumulate, bf16 out",
         "data": "synthetic (seeded normals shaped like a 5B video DiT's QKV projection)",
         "config": {"workload": "qkv_projection_x2640x3072_w9216x3072_bf16out",
                    "m": m, "k": k, "n": n, "rule": "four-over-six", "weight_blocks": "16x16",
                    "act_blocks": "1x16"},
-        "roofline": roofline,
     }
-    if not args.no_kv:
+    if "qkv" in parts:
+        log("[bench] preparing QKV projection inputs")
+        sets = linear_sets(nv, workloads, m, k, n, 3, 2)
+        log("[bench] timing the fused linear")
+        ms = bench_linear(nv, sets, args.steps, args.warmup)
+        value = flops / (ms * 1e-3) / 1e12
+        log(f"[bench] linear {ms:.4f} ms/step, {value:.1f} TFLOP/s")
+        log("[bench] timing the GEMM kernel alone")
+        gms = bench_gemm_kernel(nv, sets, max(50, args.steps // 2))
+        achieved = flops / (gms * 1e-3) / 1e12
+        result["value"] = round(value, 2)
+        result["ms_per_step"] = round(ms, 5)
+        result["roofline"] = {
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gemm_traffic(),
+            "kernel": "k_gemm_nvfp4", "kernel_ms": round(gms, 5), "algorithmic_flops_per_launch": flops,
+            "frac_of_fp4_mfma_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4)}
+        del sets
+        torch.cuda.empty_cache()
+    if "kv" in parts:
         log("[bench] KV cache quantize/dequantize")
         result["kv"] = bench_kv(nv, workloads, 30)
         torch.cuda.empty_cache()
-    if not args.no_extra:
+    if "extra" in parts:
         log("[bench] FFN and training shapes")
         result["extra"] = bench_extra(nv, workloads, 20)
         torch.cuda.empty_cache()
-    if not args.no_cpu:
+    if "cpu" in parts:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(workloads, m, k, n)
     print(json.dumps(result), flush=True)

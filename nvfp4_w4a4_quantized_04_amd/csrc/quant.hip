@@ -346,8 +346,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_col16(const uint8_t *
 
 int amax_partials(int64_t rows, int64_t cols)
 {
+    // enough workgroups to cover every CU even for small tensors: about one
+    // 16-byte vector per thread per workgroup, at most kMaxAmaxPartials
     const int64_t n = rows * cols;
-    const int64_t per_wg = (int64_t)kAmaxThreads * kAmaxUnroll * 8 * 4;   // ~4 iterations of 8-element loads
+    const int64_t per_wg = (int64_t)kAmaxThreads * 8;
     int64_t p = (n + per_wg - 1) / per_wg;
     if (p < 1) p = 1;
     if (p > kMaxAmaxPartials) p = kMaxAmaxPartials;
