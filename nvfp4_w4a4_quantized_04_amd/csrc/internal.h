@@ -9,7 +9,6 @@
 namespace nvfp4 {
 
 constexpr int kQuantThreads = 256;      // threads per quantize workgroup
-constexpr int kColGroups = 8;           // row-blocks per lane in the COL16 kernel
 constexpr int kRowBlocks = 1;           // 16-element blocks per lane in the ROW16 kernel
 constexpr int kAmaxThreads = 1024;      // threads per amax workgroup
 constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per amax thread

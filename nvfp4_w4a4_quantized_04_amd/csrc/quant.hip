@@ -11,6 +11,8 @@
 //           registers: no cross-lane traffic on the hot path.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 // Reduce the partial maxima (or read one amax) into alpha; all threads of the
@@ -52,8 +54,9 @@ __device__ __forceinline__ float absmax16B(uint4 v, float a)
     return a;
 }
 
-// Partial maxima: kAmaxThreads threads per workgroup, each keeping
-// kAmaxUnroll 16-byte loads in flight per iteration.
+// Partial maxima: workgroup w reduces one contiguous range of the tensor;
+// every thread keeps kAmaxUnroll 16-byte loads in flight per iteration (the
+// last iteration's loads are predicated, not serialized).
 template <typename T>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                        int64_t ldx, float *__restrict__ partials)
@@ -64,20 +67,24 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, 
         constexpr int V = 16 / sizeof(T);
         const int64_t n = rows * cols;
         const int64_t nv = n / V;
-        const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+        constexpr int64_t kIter = (int64_t)kAmaxThreads * kAmaxUnroll;   // vectors per workgroup iteration
+        const int64_t per_wg = ((nv + gridDim.x - 1) / gridDim.x + kIter - 1) / kIter * kIter;
+        const int64_t beg = (int64_t)blockIdx.x * per_wg;
+        const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
-        int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
-        for (; i + (kAmaxUnroll - 1) * stride < nv; i += kAmaxUnroll * stride) {
+        for (int64_t base = beg; base < end; base += kIter) {
             uint4 v[kAmaxUnroll];
 #pragma unroll
-            for (int u = 0; u < kAmaxUnroll; u++)
-                v[u] = xv[i + u * stride];
+            for (int u = 0; u < kAmaxUnroll; u++) {
+                const int64_t i = base + u * kAmaxThreads + threadIdx.x;
+                v[u] = i < end ? xv[i] : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
             for (int u = 0; u < kAmaxUnroll; u++)
                 a = absmax16B<T>(v[u], a);
         }
-        for (; i < nv; i += stride)
-            a = absmax16B<T>(xv[i], a);
+        // elements past the last whole vector
+        const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
         for (int64_t t = nv * V + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < n; t += stride)
             a = fmaxf(a, fabsf(load1(x + t)));
     } else {
@@ -151,10 +158,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
 
 // ------------------------------------------------ COL16 (1D, along rows)
 
-// Blocks of 16 consecutive rows of one column.  Each lane owns one column and
-// walks kColGroups row-blocks; consecutive lanes take consecutive columns so
-// every row load of the wave is contiguous.  Output is the ROW16 packing of
-// x^T: codes [cols][rows/2], scales [cols][rows/16].
+// Blocks of 16 consecutive rows of one column; output is the ROW16 packing of
+// x^T: codes [cols][rows/2], scales [cols][rows/16].  A workgroup owns
+// kColCols columns (two per lane) and walks groups of kColGroupRB row-blocks:
+// each wave loads the 16 rows of one row-block for its lane's two columns
+// straight into registers (the block is then lane-local), quantizes them, and
+// parks codes and scales in LDS; once a group is done the workgroup writes
+// each column's codes (8 bytes per row-block) and scales as contiguous runs.
+constexpr int kColCols = 128;                       // columns per workgroup
+constexpr int kColGroupRB = 16;                     // row-blocks per group (4 waves x 4 steps)
+constexpr int kColCodePitch = kColGroupRB * 8 + 16; // LDS bytes per column of parked codes
+
 template <typename T, bool RULE4>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                                int64_t ldx, const float *__restrict__ amax_src,
@@ -162,30 +176,90 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
                                                                uint8_t *__restrict__ scales,
                                                                float *__restrict__ alpha_out)
 {
+    constexpr int kWaves = kQuantThreads / 64;
+    constexpr int kSteps = kColGroupRB / kWaves;
     __shared__ float ktab[128];
+    __shared__ __attribute__((aligned(16))) uint8_t cpark[kColCols * kColCodePitch];
+    __shared__ __attribute__((aligned(16))) uint8_t spark[kColCols * kColGroupRB];
+
     const float alpha = block_alpha(amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
-    const int64_t c = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-    if (c >= cols)
-        return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nrb = rows / 16;
-    for (int64_t rb0 = (int64_t)blockIdx.y * kColGroups; rb0 < nrb; rb0 += (int64_t)gridDim.y * kColGroups) {
-        for (int g = 0; g < kColGroups; g++) {
-            const int64_t rb = rb0 + g;
-            if (rb >= nrb)
-                break;
-            float v[16];
-            const T *p = x + rb * 16 * ldx + c;
+    const int64_t col0 = (int64_t)blockIdx.x * kColCols;
+    const int64_t c = col0 + 2 * lane;                  // this lane's first column
+    const bool c0ok = c < cols, c1ok = c + 1 < cols;
+    // both columns in one 2-element vector load
+    const bool pair = c1ok && ldx % 2 == 0 && reinterpret_cast<uintptr_t>(x) % (2 * sizeof(T)) == 0;
+
+    // the 16 rows x 2 columns of row-block rb, as 16 packed pairs
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, uint2>::type Pair;
+    auto load_block = [&](int64_t rb, Pair (&v)[16]) {
+        const T *p = x + rb * 16 * ldx + c;
+        if (pair) {
 #pragma unroll
             for (int i = 0; i < 16; i++)
-                v[i] = load1(p + i * ldx);
-            uint32_t c0, c1, sb;
-            quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
-            *reinterpret_cast<uint2 *>(codes + c * (rows / 2) + rb * 8) = make_uint2(c0, c1);
-            scales[c * nrb + rb] = (uint8_t)sb;
+                v[i] = *reinterpret_cast<const Pair *>(p + i * ldx);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                T e[2] = {T(0), T(0)};
+                if (c0ok)
+                    e[0] = p[i * ldx];
+                if (c1ok)
+                    e[1] = p[i * ldx + 1];
+                v[i] = __builtin_bit_cast(Pair, e);
+            }
         }
+    };
+
+    for (int64_t g0 = (int64_t)blockIdx.y * kColGroupRB; g0 < nrb; g0 += (int64_t)gridDim.y * kColGroupRB) {
+        const int ng = nrb - g0 < kColGroupRB ? (int)(nrb - g0) : kColGroupRB;
+        Pair v[2][16];
+        int64_t rb = g0 + wave;
+        if (wave < ng)
+            load_block(rb, v[0]);
+#pragma unroll
+        for (int st = 0; st < kSteps; st++) {
+            const int slot = st * kWaves + wave;            // row-block index inside the group
+            if (st + 1 < kSteps && slot + kWaves < ng)
+                load_block(rb + kWaves, v[(st + 1) & 1]);
+            if (slot < ng) {
+#pragma unroll
+                for (int k = 0; k < 2; k++) {
+                    float f[16];
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        if constexpr (sizeof(T) == 2)
+                            f[i] = k == 0 ? bf16_lo(v[st & 1][i]) : bf16_hi(v[st & 1][i]);
+                        else
+                            f[i] = __uint_as_float(k == 0 ? v[st & 1][i].x : v[st & 1][i].y);
+                    }
+                    uint32_t q0, q1, sb;
+                    quant_block16<RULE4>(f, alpha, ktab, q0, q1, sb);
+                    const int cc = 2 * lane + k;
+                    *reinterpret_cast<uint2 *>(&cpark[cc * kColCodePitch + slot * 8]) = make_uint2(q0, q1);
+                    spark[cc * kColGroupRB + slot] = (uint8_t)sb;
+                }
+            }
+            rb += kWaves;
+        }
+        __syncthreads();
+        // each column's run: ng*8 code bytes, ng scale bytes
+        const int ncol = cols - col0 < kColCols ? (int)(cols - col0) : kColCols;
+        const int64_t cstride = rows / 2;
+        for (int q = tid; q < ncol * kColGroupRB; q += kQuantThreads) {
+            const int cc = q / kColGroupRB, part = q - cc * kColGroupRB;
+            if (part < ng) {
+                *reinterpret_cast<uint2 *>(codes + (col0 + cc) * cstride + g0 * 8 + part * 8) =
+                    *reinterpret_cast<const uint2 *>(&cpark[cc * kColCodePitch + part * 8]);
+                scales[(col0 + cc) * nrb + g0 + part] = spark[cc * kColGroupRB + part];
+            }
+        }
+        __syncthreads();    // the parking area is refilled by the next group
     }
 }
 
@@ -383,9 +457,15 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
         k_quant_tile16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha);
     } else {
         const int64_t nrb = rows / 16;
-        int64_t gy = (nrb + kColGroups - 1) / kColGroups;
+        // about seven resident workgroups per CU; groups spread evenly over grid.y
+        const int64_t gx = (cols + kColCols - 1) / kColCols;
+        const int64_t ngroups = (nrb + kColGroupRB - 1) / kColGroupRB;
+        const int64_t want = (1792 + gx - 1) / gx;
+        const int64_t per = (ngroups + want - 1) / want;
+        int64_t gy = (ngroups + per - 1) / per;
         if (gy > 65535) gy = 65535;
-        dim3 grid((unsigned)((cols + kQuantThreads - 1) / kQuantThreads), (unsigned)gy);
+        if (gy < 1) gy = 1;
+        dim3 grid((unsigned)gx, (unsigned)gy);
         k_quant_col16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha);
     }
 }

@@ -52,11 +52,18 @@ def test_tile16_bf16_shapes(shape, rule):
     _case(x, oracle.TILE16, rule)
 
 
-@pytest.mark.parametrize("shape", [(16, 1), (32, 50), (64, 257), (1024, 96), (2064, 130)])
+@pytest.mark.parametrize("shape", [(16, 1), (32, 50), (64, 257), (1024, 96), (2064, 130), (4144, 192), (160, 200),
+                                   (2048, 3072)])
 @pytest.mark.parametrize("rule", [0, 1])
 def test_col16_bf16_shapes(shape, rule):
     x = workloads.random_bf16(11 + shape[1] + rule, shape, 1e-3, 0.001)
     _case(x, oracle.COL16, rule)
+
+
+def test_col16_many_row_tiles():
+    # more 128-row tiles than one grid column holds: the tile loop wraps
+    x = workloads.random_bf16(12, (128 * 65535 + 48, 1), 1.0)
+    _case(x, oracle.COL16, 1)
 
 
 def test_fp32_input_and_explicit_amax():
