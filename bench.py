@@ -229,18 +229,22 @@ def bench_extra(nv, workloads, iters):
 
 
 def cpu_baseline(workloads, m, k, n):
-    """The oracle (fp32 quantizer, fp64 GEMM, OpenMP) on the full QKV step."""
+    """The oracle (fp32 quantizer, fp64 GEMM, OpenMP) on the full QKV step,
+    repeated until about 10 s of host time have passed (at most 8 steps)."""
     import oracle
     c = workloads.config2()
     W = oracle.quantize(c["w"], oracle.TILE16, oracle.FOUR_OVER_SIX)     # offline, untimed
+    steps = 0
     t0 = time.perf_counter()
-    A = oracle.quantize(c["x"], oracle.ROW16, oracle.FOUR_OVER_SIX)
-    oracle.gemm_f64(A, W)
-    dt = time.perf_counter() - t0
+    while steps < 8 and (steps == 0 or time.perf_counter() - t0 < 10.0):
+        A = oracle.quantize(c["x"], oracle.ROW16, oracle.FOUR_OVER_SIX)
+        oracle.gemm_f64(A, W)
+        steps += 1
+    dt = (time.perf_counter() - t0) / steps
     return {"value": round(2 * m * n * k / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "full QKV step: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and the "
-                      "fp64 GEMM against W [9216,3072]"}
+            "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": steps,
+            "sample": f"{steps} full QKV steps: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and "
+                      "the fp64 GEMM against W [9216,3072] (W quantized once, untimed)"}
 
 
 def main():
