@@ -12,7 +12,8 @@ The same JSON line also carries
                 against the fp16 MFMA peak (its operands are exact fp16);
   kv            NVFP4 KV-cache quantize and dequantize of K and V bf16
                 [24, 18480, 128] in GB/s of algorithmic bytes, and against HBM;
-  extra         the FFN pair and the long-sequence training shapes;
+  extra         the FFN pair and the long-sequence training shapes (forward,
+                weight gradient, data gradient);
   cpu_baseline  the CPU oracle (fp32 quantizer, fp64 GEMM) on the full QKV
                 step on the host cores.
 
@@ -224,6 +225,19 @@ def bench_extra(nv, workloads, iters):
 
     ms = time_events(wg, iters)
     out["train_wgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
+                                             "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    # data gradient dX = dY W: dY quantized along the 3072 output features, the
+    # forward's TILE16 weight transposed once in packed form (not timed)
+    w = nv.quantize((torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16), "tile16", "4over6")
+    wt = nv.transpose_tile16(w)
+    dx = torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
+    lws = nv.linear_workspace(t, n)
+
+    def dg(i):
+        nv.dgrad(dy, wt, torch.bfloat16, out=dx, workspace=lws)
+
+    ms = time_events(dg, iters)
+    out["train_dgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
                                              "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
     return out
 

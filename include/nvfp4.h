@@ -210,6 +210,25 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
                            void *dw, int dw_dtype, int64_t lddw,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * nvfp4_transpose_tile16 -- the packed transpose W^T of a tensor W [rows][cols]
+ * quantized with NVFP4_TILE16 blocks: codes_t [cols][rows/2], scales_t
+ * [cols/16][rows/16] (one byte per 16x16 tile, unchanged), alpha_t = alpha.
+ * Exact: no value is re-quantized, so dequantize(W^T) is the transpose of
+ * dequantize(W) bit for bit.  rows % 16 == 0, cols % 16 == 0; codes, scales
+ * and their transposes 16-byte aligned, must not overlap.
+ * Use: the DGRAD GEMM dX = dY W contracts W over its rows (the layer's output
+ * features); with Wt = nvfp4_transpose_tile16(W) it is
+ * nvfp4_linear(dY, ..., Wt, NVFP4_SCALE_2D, ...), the same weight quantization
+ * that FPROP uses.
+ * Source: "NVFP4 training recipe" (2D 16x16 weight blocks) and "The three
+ * GEMMs of backpropagation" (DGRAD: weight x output gradient -> activation
+ * gradient), NVFP4 Training section of the architecture walkthrough page.
+ */
+nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *alpha,
+                                      int64_t rows, int64_t cols, uint8_t *codes_t, uint8_t *scales_t,
+                                      float *alpha_t, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,7 @@ class NVFP4Error(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m nvfp4_w4a4_quantized_04_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python nvfp4_w4a4_quantized_04_amd/build.py` "
                           "(there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -65,6 +65,8 @@ def _load():
     L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_wgrad.restype = i32
     L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, P, i32, i64, P, sz, P]
+    L.nvfp4_transpose_tile16.restype = i32
+    L.nvfp4_transpose_tile16.argtypes = [P, P, P, i64, i64, P, P, P, P]
     return L
 
 
@@ -72,7 +74,7 @@ lib = _load()
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
-            "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad"]
+            "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16"]
 
 
 def _check(fn: str, st: int):
@@ -268,3 +270,24 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4ove
         _ptr(dy), _ptr(x), _dtype_code(x), t, n, k, dy.stride(0), x.stride(0), _rule(rule),
         _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def transpose_tile16(t: NVFP4Tensor, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """W^T of a 16x16-tile packed tensor, exactly (codes and scales moved, none re-quantized)."""
+    if t.block != TILE16:
+        raise ValueError("transpose_tile16 needs a TILE16 tensor")
+    _need_gpu(t.codes)
+    if out is None:
+        out = empty_packed(t.cols, t.rows, TILE16, t.codes.device)
+    _check("nvfp4_transpose_tile16", lib.nvfp4_transpose_tile16(
+        _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, _ptr(out.codes), _ptr(out.scales),
+        _ptr(out.alpha), _stream()))
+    return out
+
+
+def dgrad(dy: torch.Tensor, w_t: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4over6",
+          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """DGRAD dX = quantize(dY) @ W with w_t = transpose_tile16(W): the fused
+    linear against the transposed weight (dY quantized in 16-blocks along the
+    layer's output features, its contraction dimension)."""
+    return linear(dy, w_t, out_dtype, rule, out=out, workspace=workspace)

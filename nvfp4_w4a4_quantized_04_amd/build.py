@@ -1,6 +1,8 @@
 """Build libnvfp4.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m nvfp4_w4a4_quantized_04_amd.build
+    python nvfp4_w4a4_quantized_04_amd/build.py
+
+(run as a script: importing the package loads the library this builds)
 """
 from __future__ import annotations
 

@@ -269,4 +269,21 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
     return launch_status(launch_gemm(A, B, n_out, k_in, tokens, dw, dw_dtype, lddw, nullptr, stream));
 }
 
+nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *alpha,
+                                     int64_t rows, int64_t cols, uint8_t *codes_t, uint8_t *scales_t,
+                                     float *alpha_t, hipStream_t stream)
+{
+    if (!dims_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!alpha || !alpha_t)
+        return NVFP4_ERR_NULL;
+    if (rows > 0 && cols > 0 && (!codes || !scales || !codes_t || !scales_t))
+        return NVFP4_ERR_NULL;
+    if ((codes && !aligned16(codes)) || (codes_t && !aligned16(codes_t)) || (scales && !aligned16(scales)) ||
+        (scales_t && !aligned16(scales_t)) || ((uintptr_t)alpha & 3u) || ((uintptr_t)alpha_t & 3u))
+        return NVFP4_ERR_ALIGN;
+    return launch_status(launch_transpose_tile16(codes, scales, alpha, rows, cols, codes_t, scales_t, alpha_t,
+                                                 stream));
+}
+
 }  // extern "C"

@@ -37,6 +37,11 @@ struct GemmOperand {
     int scale2d;
 };
 
+// W^T of a 16x16-tile tensor W [rows][cols]: codes [cols][rows/2], scales
+// [cols/16][rows/16], alpha copied.  rows, cols multiples of 16.
+hipError_t launch_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                                   int64_t cols, uint8_t *codes_t, uint8_t *scales_t, float *alpha_t, hipStream_t s);
+
 // c_amax (optional): receives max |C| of the stored values
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
                        int cdtype, int64_t ldc, float *c_amax, hipStream_t s);

@@ -218,6 +218,24 @@ def gemm_f64_sampled(a: Packed, b: Packed, ms: np.ndarray, ns: np.ndarray) -> np
     return out
 
 
+def transpose_tile16(p: Packed) -> Packed:
+    """W^T of a TILE16-packed W, element by element: element (i, j) of W is
+    element (j, i) of W^T, each 16x16 tile keeps its scale byte and the tensor
+    its alpha.  Unpacks the nibbles, transposes, packs again (element 2j in
+    the low nibble)."""
+    if p.block != TILE16:
+        raise ValueError("TILE16 tensors only")
+    lo = p.codes & 0x0F
+    hi = p.codes >> 4
+    q = np.empty((p.rows, p.cols), np.uint8)
+    q[:, 0::2] = lo
+    q[:, 1::2] = hi
+    qt = np.ascontiguousarray(q.T)
+    codes = (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.ascontiguousarray(p.scales.T)
+    return Packed(codes, scales, p.alpha, p.cols, p.rows, TILE16)
+
+
 def bf16_rne(y: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bits, nearest-even (for comparing bf16 outputs)."""
     u = np.ascontiguousarray(y, np.float32).view(np.uint32).astype(np.uint64)

@@ -91,6 +91,25 @@ def test_kv_quantize_validation_without_gpu():
     assert m.lib.nvfp4_kv_quantize(FAKE, 1, 100, 128, 1, None, FAKE, FAKE, FAKE, None, 0, None) == 5
 
 
+def test_transpose_tile16_validation_without_gpu():
+    import nvfp4_w4a4_quantized_04_amd as m
+    t = m.lib.nvfp4_transpose_tile16
+    assert t(FAKE, FAKE, FAKE, 24, 32, FAKE, FAKE, FAKE, None) == 2        # rows % 16
+    assert t(FAKE, FAKE, FAKE, 32, 40, FAKE, FAKE, FAKE, None) == 2        # cols % 16
+    assert t(FAKE, FAKE, FAKE, -16, 32, FAKE, FAKE, FAKE, None) == 2
+    assert t(FAKE, FAKE, None, 32, 32, FAKE, FAKE, FAKE, None) == 1        # alpha
+    assert t(FAKE, None, FAKE, 32, 32, FAKE, FAKE, FAKE, None) == 1        # scales
+    assert t(FAKE, FAKE, FAKE, 32, 32, FAKE + 8, FAKE, FAKE, None) == 3    # codes_t alignment
+
+
+def test_hip_build_script_loads_without_the_library():
+    # the build must work on a tree where libnvfp4.so does not exist yet
+    import __graft_entry__ as ge
+    mod = ge._hip_build_module()
+    names = [os.path.basename(p) for p in mod.sources()]
+    assert {"api.hip", "gemm.hip", "quant.hip", "pack.hip"} <= set(names)
+
+
 def test_no_cpu_fallback():
     import torch
     import nvfp4_w4a4_quantized_04_amd as m

@@ -94,6 +94,28 @@ def test_training_forward_and_wgrad_full():
     _check_gemm(dw32, dw16, A, B, 55)
 
 
+def test_training_dgrad_full():
+    """DGRAD dX = dY W of the training-shaped layer: the forward's TILE16
+    weight transposed in packed form, dY [32768, 3072] quantized along the
+    output features."""
+    c = workloads.config5()
+    t, n = c["dy"].shape
+    k = c["w"].shape[1]
+    print(f"[case] dgrad t={t} n={n} k={k}", flush=True)
+    W = oracle.quantize(c["w"], oracle.TILE16, oracle.FOUR_OVER_SIX)
+    Wt = oracle.transpose_tile16(W)
+    A = oracle.quantize(c["dy"], oracle.ROW16, oracle.FOUR_OVER_SIX)
+    Wd = nv.quantize(dev_from_host(c["w"]), "tile16", "4over6")
+    Wtd = nv.transpose_tile16(Wd)
+    dyd = dev_from_host(c["dy"])
+    torch.cuda.synchronize()
+    assert_packed_equal(Wtd, Wt, "W^T tile16")
+    dx32 = nv.dgrad(dyd, Wtd, torch.float32)
+    dx16 = nv.dgrad(dyd, Wtd, torch.bfloat16)
+    torch.cuda.synchronize()
+    _check_gemm(dx32, dx16, A, Wt, 56)
+
+
 def test_kv_cache_full():
     c = workloads.config4()
     for name in ("k", "v"):

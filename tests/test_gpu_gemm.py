@@ -127,3 +127,35 @@ def test_kv_projection_amax_feeds_single_pass_kv_quantize():
     ref = oracle.quantize(host_bits(k).reshape(-1, 128), oracle.ROW16, 1)
     assert_packed_equal(t1, ref, "single pass")
     assert_packed_equal(t2, ref, "two pass")
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 160), (256, 4096), (9216, 3072), (0, 32)])
+def test_transpose_tile16_bit_exact(shape):
+    print(f"[case] transpose_tile16 {shape}", flush=True)
+    w = workloads.random_bf16(17 + shape[0], shape, 0.02)
+    W = oracle.quantize(w, oracle.TILE16, 1)
+    ref = oracle.transpose_tile16(W)
+    got = nv.transpose_tile16(packed_to_device(W))
+    torch.cuda.synchronize()
+    assert_packed_equal(got, ref, f"transpose {shape}")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 384, 512), (17, 64, 48), (1000, 1040, 272)])
+def test_dgrad(m, n, k):
+    """dX [m, k] = dY [m, n] W [n, k] through the transposed packed weight."""
+    print(f"[case] dgrad m={m} n={n} k={k}", flush=True)
+    rng = np.random.default_rng(m + n + k)
+    dy = workloads.f32_to_bf16_bits((rng.standard_normal((m, n)) * 1e-3).astype(np.float32))
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    W = oracle.quantize(w, oracle.TILE16, 1)
+    Wt = nv.transpose_tile16(packed_to_device(W))
+    dx = nv.dgrad(dev_from_host(dy), Wt, torch.float32)
+    dx16 = nv.dgrad(dev_from_host(dy), Wt, torch.bfloat16)
+    torch.cuda.synchronize()
+    A = oracle.quantize(dy, oracle.ROW16, 1)
+    ref = oracle.gemm_f64(A, oracle.transpose_tile16(W))
+    assert rel_frobenius(host_bits(dx), ref) <= GEMM_RTOL
+    assert np.array_equal(host_bits(dx16), oracle.bf16_rne(host_bits(dx)))
+    # the same product on the dequantized values in the original orientation
+    ref2 = oracle.dequantize(A).astype(np.float64) @ oracle.dequantize(W).astype(np.float64)
+    assert rel_frobenius(host_bits(dx), ref2) <= GEMM_RTOL

@@ -355,3 +355,35 @@ def test_amax_argument_overrides():
     am = float(np.abs(x).max()) * 2
     p = oracle.quantize(x, ROW16, FOUR_OVER_SIX, amax=am)
     assert p.alpha == oracle.global_scale(am)
+
+
+def test_tile16_transpose_is_exact():
+    # the packed transpose moves every element and tile scale: dequantize
+    # commutes with it, and two transposes are the identity
+    x = _rand(13, (64, 96))
+    p = oracle.quantize(x, TILE16, FOUR_OVER_SIX)
+    t = oracle.transpose_tile16(p)
+    assert (t.rows, t.cols) == (96, 64)
+    assert np.array_equal(oracle.dequantize(t).view(np.uint32), oracle.dequantize(p).T.copy().view(np.uint32))
+    tt = oracle.transpose_tile16(t)
+    assert np.array_equal(tt.codes, p.codes) and np.array_equal(tt.scales, p.scales)
+    # one planted element lands at the transposed place
+    y = np.zeros((32, 48), np.float32)
+    y[3, 40] = 2688.0               # alpha = 1: both values are exactly representable
+    y[0, 0] = -3.0
+    q = oracle.transpose_tile16(oracle.quantize(y, TILE16, FOUR_OVER_SIX))
+    d = oracle.dequantize(q)
+    assert d[40, 3] == np.float32(2688.0) and d[0, 0] == np.float32(-3.0) and np.count_nonzero(d) == 2
+
+
+def test_tile16_quantize_of_transpose_matches_transpose_on_exact_blocks():
+    # a tile's scale and codes do not depend on the orientation; only the
+    # fp32 order of the 6-vs-4 error sum does, and exactly representable
+    # tiles have no near ties
+    rng = np.random.default_rng(14)
+    q = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    x = q[rng.integers(0, 8, (48, 64))] * rng.choice([-1, 1], (48, 64)).astype(np.float32)
+    x[0, 0] = 2688.0
+    a = oracle.transpose_tile16(oracle.quantize(x, TILE16, FOUR_OVER_SIX))
+    b = oracle.quantize(np.ascontiguousarray(x.T), TILE16, FOUR_OVER_SIX)
+    assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales) and a.alpha == b.alpha
