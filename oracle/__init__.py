@@ -77,6 +77,10 @@ def lib():
         L.nvo_quantize.restype = None
         L.nvo_quantize_exact_reading.argtypes = [P, i64, i64, i64, ctypes.c_int, ctypes.c_int, P, P, P]
         L.nvo_quantize_exact_reading.restype = None
+        L.nvo_rht16.argtypes = [P, ctypes.c_uint]
+        L.nvo_rht16.restype = None
+        L.nvo_quantize_col16_rht.argtypes = [P, i64, i64, i64, ctypes.c_int, ctypes.c_uint, P, P, P, P, P]
+        L.nvo_quantize_col16_rht.restype = None
         L.nvo_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int, P, i64]
         L.nvo_dequantize.restype = None
         L.nvo_gemm_f64.argtypes = [P, P, ctypes.c_float, ctypes.c_int, P, P, ctypes.c_float,
@@ -169,6 +173,32 @@ def quantize(x: np.ndarray, block: int = ROW16, rule: int = FOUR_OVER_SIX, amax=
     lib().nvo_quantize(_ptr(x), rows, cols, cols, block, rule,
                        None if am is None else _ptr(am), _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(stats))
     return Packed(codes, scales, alpha[0], rows, cols, block, stats)
+
+
+def rht16(v: np.ndarray, signs: int) -> np.ndarray:
+    """The 16-point random Hadamard transform of one block (fp32 steps of the
+    C oracle); returns a new array."""
+    out = np.ascontiguousarray(v, dtype=np.float32).copy()
+    assert out.shape == (16,)
+    lib().nvo_rht16(_ptr(out), signs & 0xFFFF)
+    return out
+
+
+def quantize_col16_rht(x: np.ndarray, signs: int, rule: int = FOUR_OVER_SIX, amax=None) -> Packed:
+    """COL16 quantization of the tensor with every 16-row column block
+    transformed by rht16 (the WGRAD operand path)."""
+    x = _as_f32(x)
+    rows, cols = x.shape
+    cs, ss = packed_shapes(rows, cols, COL16)
+    codes = np.zeros(cs, np.uint8)
+    scales = np.zeros(ss, np.uint8)
+    alpha = np.zeros(1, np.float32)
+    stats = np.zeros(2, np.int64)
+    am = None if amax is None else np.array([amax], np.float32)
+    lib().nvo_quantize_col16_rht(_ptr(x), rows, cols, cols, rule, signs & 0xFFFF,
+                                 None if am is None else _ptr(am), _ptr(codes), _ptr(scales), _ptr(alpha),
+                                 _ptr(stats))
+    return Packed(codes, scales, alpha[0], rows, cols, COL16, stats)
 
 
 def quantize_exact_reading(x: np.ndarray, block: int = ROW16, rule: int = FOUR_OVER_SIX) -> Packed:

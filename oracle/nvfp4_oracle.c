@@ -311,6 +311,60 @@ void nvo_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld, int bl
     }
 }
 
+/* ------------------------------------------------ random Hadamard transform */
+
+/* The random Hadamard transform applied to the WGRAD operands before
+ * quantization (architecture walkthrough page, NVFP4 Training section,
+ * "Random Hadamard Transform (RHT) for gradient stabilization"): both
+ * operands are multiplied by one fixed orthogonal matrix along the reduction
+ * (token) axis, so dW = (R dY)^T (R X) = dY^T X before quantization.
+ *
+ * Reading (the pages give neither size nor construction): R = (1/4) H16 D on
+ * every 16-element block of a column along the tokens, the blocks of the COL16
+ * quantization; H16 the Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i&j)),
+ * D = diag(d_i) with d_i = -1 where bit i of `signs` is set.  fp32 evaluation
+ * order: flip the signs, then the butterfly stages h = 1, 2, 4, 8, each
+ * replacing (v[i], v[i+h]) for i & h == 0 by (v[i] + v[i+h], v[i] - v[i+h])
+ * (one rounding each), then multiply by 0.25. */
+void nvo_rht16(float *v, unsigned signs)
+{
+    for (int i = 0; i < 16; i++)
+        if ((signs >> i) & 1u)
+            v[i] = -v[i];
+    for (int h = 1; h < 16; h <<= 1)
+        for (int i = 0; i < 16; i++)
+            if (!(i & h)) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    for (int i = 0; i < 16; i++)
+        v[i] = v[i] * 0.25f;
+}
+
+/* COL16 quantization of R x: x [rows][cols] (ld), rows % 16 == 0.  The
+ * transformed tensor is formed first, then quantized exactly as nvo_quantize
+ * does (its amax is that of R x). */
+void nvo_quantize_col16_rht(const float *x, int64_t rows, int64_t cols, int64_t ld, int rule, unsigned signs,
+                            const float *amax_in, uint8_t *codes, uint8_t *scales, float *alpha_out,
+                            int64_t *stats)
+{
+    float *t = (float *)malloc((size_t)(rows * cols > 0 ? rows * cols : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++) {
+        float v[16];
+        for (int64_t rb = 0; rb < rows / 16; rb++) {
+            for (int i = 0; i < 16; i++)
+                v[i] = x[(rb * 16 + i) * ld + c];
+            nvo_rht16(v, signs);
+            for (int i = 0; i < 16; i++)
+                t[(rb * 16 + i) * cols + c] = v[i];
+        }
+    }
+    nvo_quantize(t, rows, cols, cols, NVO_COL16, rule, amax_in, codes, scales, alpha_out, stats);
+    free(t);
+}
+
 /* Dequantize to fp32 y [rows][cols] (original orientation, row stride ldy):
  * xhat = RN32(RN32(q * s) * alpha). */
 void nvo_dequantize(const uint8_t *codes, const uint8_t *scales, float alpha, int64_t rows,

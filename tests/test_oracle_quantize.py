@@ -387,3 +387,75 @@ def test_tile16_quantize_of_transpose_matches_transpose_on_exact_blocks():
     a = oracle.transpose_tile16(oracle.quantize(x, TILE16, FOUR_OVER_SIX))
     b = oracle.quantize(np.ascontiguousarray(x.T), TILE16, FOUR_OVER_SIX)
     assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales) and a.alpha == b.alpha
+
+
+def _hadamard16():
+    i = np.arange(16)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+@pytest.mark.parametrize("signs", [0x0000, 0xFFFF, 0xA5C3, 0x0001])
+def test_rht16_integer_inputs_match_the_matrix(signs):
+    # integer inputs: every butterfly sum is exact, so the fp32 result is the
+    # matrix product (1/4) H16 D x itself
+    rng = np.random.default_rng(signs)
+    H = _hadamard16()
+    d = np.array([-1 if (signs >> i) & 1 else 1 for i in range(16)], np.int64)
+    for _ in range(20):
+        x = rng.integers(-1000, 1000, 16)
+        want = (H @ (d * x)).astype(np.float64) / 4.0
+        got = oracle.rht16(x.astype(np.float32), signs)
+        assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_rht16_is_orthogonal_and_bounded():
+    rng = np.random.default_rng(31)
+    H = _hadamard16().astype(np.float64)
+    signs = 0x5A0F
+    d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    for _ in range(50):
+        x = (rng.standard_normal(16) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        y = oracle.rht16(x, signs)
+        exact = H @ (d * x.astype(np.float64)) / 4.0
+        # four rounded stages: each adds at most 2^-24 of a partial sum <= sum |x|
+        assert np.max(np.abs(y - exact)) <= 4 * 2.0 ** -24 * np.sum(np.abs(x))
+        # norm preserved up to rounding; no output beyond sum |x| / 4
+        assert abs(np.linalg.norm(y.astype(np.float64)) - np.linalg.norm(x.astype(np.float64))) <= \
+            1e-6 * np.linalg.norm(x.astype(np.float64))
+        assert np.max(np.abs(y)) <= np.sum(np.abs(x.astype(np.float64))) / 4.0 * (1 + 1e-6)
+    # the inverse (D H / 4) undoes it exactly on integers
+    x = rng.integers(-500, 500, 16).astype(np.float32)
+    back = oracle.rht16(oracle.rht16(x, signs), 0)
+    back = np.where(d < 0, -back, back)
+    assert np.array_equal(back, x)
+
+
+def test_col16_rht_quantizes_the_transformed_tensor():
+    x = _rand(32, (64, 40))
+    signs = 0x9C31
+    t = np.empty_like(x)
+    for c in range(x.shape[1]):
+        for rb in range(x.shape[0] // 16):
+            t[rb * 16:(rb + 1) * 16, c] = oracle.rht16(x[rb * 16:(rb + 1) * 16, c], signs)
+    a = oracle.quantize_col16_rht(x, signs)
+    b = oracle.quantize(t, COL16, FOUR_OVER_SIX)
+    assert np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales) and a.alpha == b.alpha
+
+
+def test_rht_wgrad_product_unchanged_before_quantization():
+    # (R dY)^T (R X) = dY^T X: checked on the transformed fp32 tensors in fp64
+    rng = np.random.default_rng(33)
+    dy = rng.standard_normal((48, 24)).astype(np.float32)
+    x = rng.standard_normal((48, 20)).astype(np.float32)
+    signs = 0x3E91
+
+    def rot(m):
+        out = np.empty_like(m)
+        for c in range(m.shape[1]):
+            for rb in range(m.shape[0] // 16):
+                out[rb * 16:(rb + 1) * 16, c] = oracle.rht16(m[rb * 16:(rb + 1) * 16, c], signs)
+        return out.astype(np.float64)
+    got = rot(dy).T @ rot(x)
+    want = dy.astype(np.float64).T @ x.astype(np.float64)
+    assert np.max(np.abs(got - want)) <= 1e-5 * np.max(np.abs(want))
