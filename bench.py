@@ -226,6 +226,13 @@ def bench_extra(nv, workloads, iters):
     ms = time_events(wg, iters)
     out["train_wgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
                                              "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    # the same with the random Hadamard transform on both operands
+    def wgr(i):
+        nv.wgrad(dy, x, torch.bfloat16, out=dw, workspace=ws, rht_signs=0xC39A)
+
+    ms = time_events(wgr, iters)
+    out["train_wgrad_rht_t32768_n3072_k3072"] = {"ms": round(ms, 4),
+                                                 "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
     # data gradient dX = dY W: dY quantized along the 3072 output features, the
     # forward's TILE16 weight transposed once in packed form (not timed)
     w = nv.quantize((torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16), "tile16", "4over6")

@@ -201,14 +201,42 @@ size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in);
  * `rule`, amax of each computed on the device).  dy [tokens][n_out] (ld lddy),
  * x [tokens][k_in] (ld ldx), same dtype; tokens % 16 == 0.  dW [n_out][k_in]
  * (ld lddw), fp32 or bf16.
+ * rht_signs: -1 quantizes dY and X as they are; 0..0xFFFF first applies the
+ * random Hadamard transform with these signs to both, along the tokens (see
+ * nvfp4_quantize_col16_rht), so dW is computed from R dY and R X.
  * Source: "The three GEMMs of backpropagation" (WGRAD: activation x output
  * gradient -> weight gradient) with 1D gradient blocks along the reduction
- * dimension ("NVFP4 training recipe").
+ * dimension ("NVFP4 training recipe"), and "Random Hadamard Transform (RHT)
+ * for gradient stabilization" for the optional transform.
  */
 nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out,
-                           int64_t k_in, int64_t lddy, int64_t ldx, int rule,
+                           int64_t k_in, int64_t lddy, int64_t ldx, int rule, int rht_signs,
                            void *dw, int dw_dtype, int64_t lddw,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_col16_rht -- NVFP4_COL16 quantization of R x, where R applies
+ * the random Hadamard transform to every 16-row block of every column (the
+ * COL16 blocks): R = (1/4) H16 D, H16 the Sylvester Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)), D = diag(-1 where bit i of rht_signs is
+ * set, else +1), rht_signs in [0, 0xFFFF].  fp32 order of the transform:
+ * sign flips, butterfly stages h = 1, 2, 4, 8 mapping (v[i], v[i+h]) with
+ * i & h == 0 to (v[i] + v[i+h], v[i] - v[i+h]), then * 0.25.  alpha and the
+ * codes are those of the transformed tensor; amax NULL computes its max |R x|
+ * (one extra read of x), else a device pointer to it.  Other arguments and
+ * layouts as nvfp4_quantize with NVFP4_COL16.  R is orthogonal, so a GEMM of
+ * two operands transformed with the same signs contracts to the product of
+ * the untransformed ones (up to quantization).
+ * Source: "Random Hadamard Transform (RHT) for gradient stabilization"
+ * (NVFP4 Training section of the architecture walkthrough page): both WGRAD
+ * operands are multiplied by one fixed random Hadamard matrix before
+ * quantization.  Size 16, aligned with the quantization blocks, and the
+ * construction above are this library's reading (the pages give neither).
+ */
+nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                        int rule, int rht_signs, const float *amax,
+                                        uint8_t *codes, uint8_t *scales, float *alpha,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nvfp4_transpose_tile16 -- the packed transpose W^T of a tensor W [rows][cols]

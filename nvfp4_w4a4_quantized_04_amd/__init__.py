@@ -64,7 +64,9 @@ def _load():
     L.nvfp4_wgrad_workspace_size.restype = sz
     L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_wgrad.restype = i32
-    L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, P, i32, i64, P, sz, P]
+    L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, i32, P, i32, i64, P, sz, P]
+    L.nvfp4_quantize_col16_rht.restype = i32
+    L.nvfp4_quantize_col16_rht.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_transpose_tile16.restype = i32
     L.nvfp4_transpose_tile16.argtypes = [P, P, P, i64, i64, P, P, P, P]
     return L
@@ -74,7 +76,8 @@ lib = _load()
 
 EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
-            "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16"]
+            "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
+            "nvfp4_quantize_col16_rht"]
 
 
 def _check(fn: str, st: int):
@@ -255,8 +258,10 @@ def wgrad_workspace(tokens: int, n_out: int, k_in: int, device="cuda") -> torch.
 
 
 def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4over6",
-          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """dW = dY^T X with both operands NVFP4-quantized along the token axis."""
+          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+          rht_signs: int | None = None) -> torch.Tensor:
+    """dW = dY^T X with both operands NVFP4-quantized along the token axis;
+    rht_signs (0..0xFFFF) first applies the random Hadamard transform to both."""
     _need_gpu(dy, x)
     t, n = dy.shape
     t2, k = x.shape
@@ -268,7 +273,8 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4ove
         workspace = wgrad_workspace(t, n, k, x.device)
     _check("nvfp4_wgrad", lib.nvfp4_wgrad(
         _ptr(dy), _ptr(x), _dtype_code(x), t, n, k, dy.stride(0), x.stride(0), _rule(rule),
-        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
+        -1 if rht_signs is None else int(rht_signs), _ptr(out), _out_dtype_code(out.dtype), out.stride(0),
+        _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
@@ -291,3 +297,22 @@ def dgrad(dy: torch.Tensor, w_t: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4o
     linear against the transposed weight (dY quantized in 16-blocks along the
     layer's output features, its contraction dimension)."""
     return linear(dy, w_t, out_dtype, rule, out=out, workspace=workspace)
+
+
+def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.Tensor | None = None,
+                       out: NVFP4Tensor | None = None, workspace: torch.Tensor | None = None) -> NVFP4Tensor:
+    """COL16 quantization of the tensor after the 16-point random Hadamard
+    transform of every column block (signs: 16-bit mask of the diagonal)."""
+    _need_gpu(x, amax)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = empty_packed(rows, cols, COL16, x.device)
+    if workspace is None and amax is None:
+        workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
+    _check("nvfp4_quantize_col16_rht", lib.nvfp4_quantize_col16_rht(
+        _ptr(x), _dtype_code(x), rows, cols, x.stride(0), _rule(rule), int(signs), _ptr(amax), _ptr(out.codes),
+        _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream()))
+    return out

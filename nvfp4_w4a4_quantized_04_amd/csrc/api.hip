@@ -49,22 +49,29 @@ nvfp4_status_t check_quant_args(const void *x, int x_dtype, int64_t rows, int64_
 }
 
 // Quantize with the amax pass when no amax is given; ws holds the partials.
+// rht_signs >= 0: COL16 blocks go through the random Hadamard transform first
+// (the amax pass then measures the transformed tensor).
 nvfp4_status_t do_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
                            const float *amax, uint8_t *codes, uint8_t *scales, float *alpha, float *partials,
-                           hipStream_t stream)
+                           hipStream_t stream, int rht_signs = -1)
 {
     const float *src = amax;
     int n = 1;
     if (!amax) {
         n = amax_partials(rows, cols);
-        hipError_t e = launch_amax(x, x_dtype, rows, cols, ldx, partials, n, stream);
+        hipError_t e = rht_signs >= 0
+                           ? launch_amax_col16_rht(x, x_dtype, rows, cols, ldx, (uint32_t)rht_signs, partials, n,
+                                                   stream)
+                           : launch_amax(x, x_dtype, rows, cols, ldx, partials, n, stream);
         if (e != hipSuccess)
             return NVFP4_ERR_LAUNCH;
         src = partials;
     }
     return launch_status(launch_quantize(x, x_dtype, rows, cols, ldx, block, rule, src, n, codes, scales, alpha,
-                                         stream));
+                                         stream, rht_signs));
 }
+
+inline bool signs_ok(int s) { return s >= -1 && s <= 0xFFFF; }
 
 bool operand_ok(const uint8_t *codes, const uint8_t *scales, const float *alpha, int layout, int64_t rows,
                 int64_t k)
@@ -232,10 +239,10 @@ size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in)
 }
 
 nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out, int64_t k_in,
-                           int64_t lddy, int64_t ldx, int rule, void *dw, int dw_dtype, int64_t lddw,
+                           int64_t lddy, int64_t ldx, int rule, int rht_signs, void *dw, int dw_dtype, int64_t lddw,
                            void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (!dtype_ok(dtype) || !dtype_ok(dw_dtype) || !rule_ok(rule))
+    if (!dtype_ok(dtype) || !dtype_ok(dw_dtype) || !rule_ok(rule) || !signs_ok(rht_signs))
         return NVFP4_ERR_DTYPE;
     if (!dims_ok(tokens, n_out) || !dims_ok(k_in, 1) || tokens % 16 != 0 || lddy < n_out || ldx < k_in ||
         lddw < k_in)
@@ -258,10 +265,11 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
     uint8_t *c_x = s_dy + round_up((size_t)(n_out * tokens / 16), kAlignWs);
     uint8_t *s_x = c_x + round_up((size_t)(k_in * tokens / 2), kAlignWs);
     nvfp4_status_t st = do_quantize(dy, dtype, tokens, n_out, lddy, NVFP4_COL16, rule, nullptr, c_dy, s_dy,
-                                    alpha_dy, part_dy, stream);
+                                    alpha_dy, part_dy, stream, rht_signs);
     if (st != NVFP4_OK)
         return st;
-    st = do_quantize(x, dtype, tokens, k_in, ldx, NVFP4_COL16, rule, nullptr, c_x, s_x, alpha_x, part_x, stream);
+    st = do_quantize(x, dtype, tokens, k_in, ldx, NVFP4_COL16, rule, nullptr, c_x, s_x, alpha_x, part_x, stream,
+                     rht_signs);
     if (st != NVFP4_OK)
         return st;
     GemmOperand A{c_dy, s_dy, alpha_dy, NVFP4_SCALE_1D};
@@ -284,6 +292,25 @@ nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scale
         return NVFP4_ERR_ALIGN;
     return launch_status(launch_transpose_tile16(codes, scales, alpha, rows, cols, codes_t, scales_t, alpha_t,
                                                  stream));
+}
+
+nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                       int rule, int rht_signs, const float *amax, uint8_t *codes, uint8_t *scales,
+                                       float *alpha, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!signs_ok(rht_signs) || rht_signs < 0)
+        return NVFP4_ERR_DTYPE;
+    nvfp4_status_t st = check_quant_args(x, x_dtype, rows, cols, ldx, NVFP4_COL16, rule, codes, scales, alpha);
+    if (st != NVFP4_OK)
+        return st;
+    if (!amax) {
+        if (!workspace || workspace_bytes < nvfp4_quantize_workspace_size(rows, cols))
+            return NVFP4_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return NVFP4_ERR_ALIGN;
+    }
+    return do_quantize(x, x_dtype, rows, cols, ldx, NVFP4_COL16, rule, amax, codes, scales, alpha,
+                       (float *)workspace, stream, rht_signs);
 }
 
 }  // extern "C"

@@ -185,6 +185,32 @@ __device__ __forceinline__ void load16(const float *p, float (&x)[16])
 __device__ __forceinline__ float load1(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 
+// Random Hadamard transform of one 16-element block along the reduction axis
+// (NVFP4 Training section, "Random Hadamard Transform (RHT) for gradient
+// stabilization"): x <- (1/4) H16 D x, D = diag(-1 where bit i of signs is
+// set).  fp32 order: sign flips, butterfly stages h = 1, 2, 4, 8 with
+// (a, b) -> (a + b, a - b), then the exact scaling by 1/4.
+__device__ __forceinline__ void rht16(float (&x)[16], uint32_t signs)
+{
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        x[i] = ((signs >> i) & 1u) ? -x[i] : x[i];
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            if (i & h)
+                continue;
+            const float a = x[i], b = x[i + h];
+            x[i] = a + b;
+            x[i + h] = a - b;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        x[i] = x[i] * 0.25f;
+}
+
 // Wave-wide max (64 lanes).
 __device__ __forceinline__ float wave_max(float v)
 {

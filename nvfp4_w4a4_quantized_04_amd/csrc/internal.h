@@ -22,10 +22,15 @@ int amax_partials(int64_t rows, int64_t cols);
 hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
                        int n_partials, hipStream_t s);
 
+// amax partials of the COL16 blocks after the random Hadamard transform
+hipError_t launch_amax_col16_rht(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t signs,
+                                 float *partials, int n_partials, hipStream_t s);
+
 // amax_src: n_amax partial maxima (n_amax > 1) or one amax (n_amax == 1).
+// rht_signs >= 0 (COL16 only): transform every block first (signs in bits 0-15).
 hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
                            const float *amax_src, int n_amax, uint8_t *codes, uint8_t *scales, float *alpha,
-                           hipStream_t s);
+                           hipStream_t s, int rht_signs = -1);
 
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
                              int64_t cols, int block, void *y, int ydtype, int64_t ldy, hipStream_t s);

@@ -169,12 +169,12 @@ constexpr int kColCols = 128;                       // columns per workgroup
 constexpr int kColGroupRB = 16;                     // row-blocks per group (4 waves x 4 steps)
 constexpr int kColCodePitch = kColGroupRB * 8 + 16; // LDS bytes per column of parked codes
 
-template <typename T, bool RULE4>
+template <typename T, bool RULE4, bool RHT>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                                int64_t ldx, const float *__restrict__ amax_src,
                                                                int n_amax, uint8_t *__restrict__ codes,
                                                                uint8_t *__restrict__ scales,
-                                                               float *__restrict__ alpha_out)
+                                                               float *__restrict__ alpha_out, uint32_t signs)
 {
     constexpr int kWaves = kQuantThreads / 64;
     constexpr int kSteps = kColGroupRB / kWaves;
@@ -238,6 +238,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
                         else
                             f[i] = __uint_as_float(k == 0 ? v[st & 1][i].x : v[st & 1][i].y);
                     }
+                    if (RHT)
+                        rht16(f, signs);
                     uint32_t q0, q1, sb;
                     quant_block16<RULE4>(f, alpha, ktab, q0, q1, sb);
                     const int cc = 2 * lane + k;
@@ -260,6 +262,67 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
             }
         }
         __syncthreads();    // the parking area is refilled by the next group
+    }
+}
+
+// amax of the transformed COL16 blocks: each lane takes a pair of columns and
+// one row-block per task (16 rows, consecutive lanes on consecutive pairs).
+template <typename T>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_col16_rht(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                                 int64_t ldx, uint32_t signs,
+                                                                 float *__restrict__ partials)
+{
+    __shared__ float red[kAmaxThreads / 64];
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, uint2>::type Pair;
+    const int64_t pairs = (cols + 1) / 2, nrb = rows / 16;
+    const int64_t tasks = pairs * nrb;
+    const bool vec = cols % 2 == 0 && ldx % 2 == 0 && reinterpret_cast<uintptr_t>(x) % (2 * sizeof(T)) == 0;
+    float a = 0.0f;
+    for (int64_t t = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < tasks;
+         t += (int64_t)gridDim.x * kAmaxThreads) {
+        const int64_t rb = t / pairs, cp = t - rb * pairs;
+        const int64_t c = 2 * cp;
+        const T *p = x + rb * 16 * ldx + c;
+        Pair v[16];
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                v[i] = *reinterpret_cast<const Pair *>(p + i * ldx);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                T e[2] = {p[i * ldx], T(0)};
+                if (c + 1 < cols)
+                    e[1] = p[i * ldx + 1];
+                v[i] = __builtin_bit_cast(Pair, e);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            float f[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                if constexpr (sizeof(T) == 2)
+                    f[i] = k == 0 ? bf16_lo(v[i]) : bf16_hi(v[i]);
+                else
+                    f[i] = __uint_as_float(k == 0 ? v[i].x : v[i].y);
+            }
+            rht16(f, signs);
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                a = fmaxf(a, fabsf(f[i]));
+        }
+    }
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+#pragma unroll
+        for (int w = 1; w < kAmaxThreads / 64; w++)
+            b = fmaxf(b, red[w]);
+        partials[blockIdx.x] = b;
     }
 }
 
@@ -442,7 +505,7 @@ hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int
 
 template <typename T, bool R4>
 static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, int block, const float *amax_src,
-                           int n_amax, uint8_t *codes, uint8_t *scales, float *alpha, hipStream_t s)
+                           int n_amax, uint8_t *codes, uint8_t *scales, float *alpha, hipStream_t s, int rht_signs)
 {
     if (block == 0) {
         const int64_t bpr = cols / 16;
@@ -466,13 +529,18 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
         if (gy > 65535) gy = 65535;
         if (gy < 1) gy = 1;
         dim3 grid((unsigned)gx, (unsigned)gy);
-        k_quant_col16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha);
+        if (rht_signs >= 0)
+            k_quant_col16<T, R4, true><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes,
+                                                                      scales, alpha, (uint32_t)rht_signs);
+        else
+            k_quant_col16<T, R4, false><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes,
+                                                                       scales, alpha, 0u);
     }
 }
 
 hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int block, int rule,
                            const float *amax_src, int n_amax, uint8_t *codes, uint8_t *scales, float *alpha,
-                           hipStream_t s)
+                           hipStream_t s, int rht_signs)
 {
     if (rows == 0 || cols == 0) {
         // nothing to encode; alpha still follows the rule (amax 0 -> 1)
@@ -481,12 +549,24 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
         return hipGetLastError();
     }
     if (dtype == 1) {
-        if (rule) launch_quant_t<uint16_t, true>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
-        else      launch_quant_t<uint16_t, false>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+        if (rule) launch_quant_t<uint16_t, true>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s, rht_signs);
+        else      launch_quant_t<uint16_t, false>((const uint16_t *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s, rht_signs);
     } else {
-        if (rule) launch_quant_t<float, true>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
-        else      launch_quant_t<float, false>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s);
+        if (rule) launch_quant_t<float, true>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s, rht_signs);
+        else      launch_quant_t<float, false>((const float *)x, rows, cols, ldx, block, amax_src, n_amax, codes, scales, alpha, s, rht_signs);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_col16_rht(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t signs,
+                                 float *partials, int n_partials, hipStream_t s)
+{
+    if (dtype == 1)
+        k_amax_col16_rht<uint16_t><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, signs,
+                                                                       partials);
+    else
+        k_amax_col16_rht<float><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, signs,
+                                                                    partials);
     return hipGetLastError();
 }
 

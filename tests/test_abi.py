@@ -82,7 +82,13 @@ def test_gemm_and_linear_validation_without_gpu():
     assert need >= 32 * 64 * 9 // 16
     assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None, FAKE + 16, need, None) == 3
     w = m.lib.nvfp4_wgrad
-    assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
+    assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, -1, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
+    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, 0x10000, FAKE, 0, 32, FAKE, 1 << 30, None) == 4  # signs
+    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, -2, FAKE, 0, 32, FAKE, 1 << 30, None) == 4
+    r = m.lib.nvfp4_quantize_col16_rht
+    assert r(FAKE, 1, 32, 32, 32, 1, -1, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 4     # transform required
+    assert r(FAKE, 1, 24, 32, 32, 1, 7, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2      # rows % 16
+    assert r(FAKE, 1, 32, 32, 32, 1, 7, None, FAKE, FAKE, FAKE, None, 0, None) == 5         # workspace
 
 
 def test_kv_quantize_validation_without_gpu():

@@ -94,6 +94,27 @@ def test_training_forward_and_wgrad_full():
     _check_gemm(dw32, dw16, A, B, 55)
 
 
+def test_training_wgrad_rht_full():
+    """WGRAD with the random Hadamard transform on both operands, full size."""
+    c = workloads.config5()
+    signs = 0xC39A
+    t, n = c["dy"].shape
+    k = c["x"].shape[1]
+    print(f"[case] wgrad rht t={t} n={n} k={k}", flush=True)
+    A = oracle.quantize_col16_rht(c["dy"], signs, oracle.FOUR_OVER_SIX)
+    B = oracle.quantize_col16_rht(c["x"], signs, oracle.FOUR_OVER_SIX)
+    dyd, xd = dev_from_host(c["dy"]), dev_from_host(c["x"])
+    Ad = nv.quantize_col16_rht(dyd, signs, "4over6")
+    Bd = nv.quantize_col16_rht(xd, signs, "4over6")
+    torch.cuda.synchronize()
+    assert_packed_equal(Ad, A, "R dY col16")
+    assert_packed_equal(Bd, B, "R X col16")
+    dw32 = nv.wgrad(dyd, xd, torch.float32, rht_signs=signs)
+    dw16 = nv.wgrad(dyd, xd, torch.bfloat16, rht_signs=signs)
+    torch.cuda.synchronize()
+    _check_gemm(dw32, dw16, A, B, 57)
+
+
 def test_training_dgrad_full():
     """DGRAD dX = dY W of the training-shaped layer: the forward's TILE16
     weight transposed in packed form, dY [32768, 3072] quantized along the

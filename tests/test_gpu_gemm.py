@@ -97,6 +97,23 @@ def test_wgrad_col16():
     assert rel_frobenius(host_bits(dw), ref) <= GEMM_RTOL
 
 
+def test_wgrad_col16_rht():
+    rng = np.random.default_rng(24)
+    t, n, k = 1040, 96, 160
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((t, k)).astype(np.float32))
+    dy = workloads.f32_to_bf16_bits((rng.standard_normal((t, n)) * 1e-3).astype(np.float32))
+    signs = 0x6D2B
+    dw = nv.wgrad(dev_from_host(dy), dev_from_host(x), torch.float32, rht_signs=signs)
+    torch.cuda.synchronize()
+    A = oracle.quantize_col16_rht(dy, signs, 1)
+    B = oracle.quantize_col16_rht(x, signs, 1)
+    ref = oracle.gemm_f64(A, B)
+    assert rel_frobenius(host_bits(dw), ref) <= GEMM_RTOL
+    # the transform cancels in the product: close to the unquantized dY^T X
+    exact = workloads.bf16_to_f32(dy).astype(np.float64).T @ workloads.bf16_to_f32(x).astype(np.float64)
+    assert rel_frobenius(host_bits(dw), exact) < 0.2
+
+
 def test_epilogue_amax_output():
     """c_amax / y_amax equal max |C| of the stored outputs (fp32 and bf16)."""
     c = workloads.config2(m=300, k=512, n=384)

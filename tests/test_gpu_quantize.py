@@ -66,6 +66,33 @@ def test_col16_many_row_tiles():
     _case(x, oracle.COL16, 1)
 
 
+@pytest.mark.parametrize("shape", [(16, 1), (64, 257), (2064, 130), (4144, 192), (2048, 3072)])
+@pytest.mark.parametrize("signs", [0x0000, 0xB6E3])
+def test_col16_rht_bf16_shapes(shape, signs):
+    print(f"[case] col16 rht shape={shape} signs={signs:#06x}", flush=True)
+    x = workloads.random_bf16(19 + shape[1] + signs, shape, 1.0, 0.001)
+    ref = oracle.quantize_col16_rht(x, signs, 1)
+    got = nv.quantize_col16_rht(dev_from_host(x), signs, "4over6")
+    torch.cuda.synchronize()
+    assert_packed_equal(got, ref, f"col16 rht {shape} {signs:#x}")
+
+
+def test_col16_rht_fp32_and_explicit_amax():
+    rng = np.random.default_rng(20)
+    x = (rng.standard_normal((96, 80)) * 5).astype(np.float32)
+    x[7, 3] = 400.0                                  # an outlier the transform spreads over its block
+    signs = 0x1F2E
+    ref = oracle.quantize_col16_rht(x, signs, 1)
+    got = nv.quantize_col16_rht(dev_from_host(x), signs, "4over6")
+    am = float(ref.alpha) * 2688.0 * 1.5
+    ref2 = oracle.quantize_col16_rht(x, signs, 1, amax=am)
+    got2 = nv.quantize_col16_rht(dev_from_host(x), signs, "4over6",
+                                 amax=torch.tensor([am], dtype=torch.float32).cuda())
+    torch.cuda.synchronize()
+    assert_packed_equal(got, ref, "col16 rht fp32")
+    assert_packed_equal(got2, ref2, "col16 rht fp32 amax")
+
+
 def test_fp32_input_and_explicit_amax():
     rng = np.random.default_rng(5)
     x = (rng.standard_normal((64, 256)) * 3).astype(np.float32)
