@@ -187,6 +187,9 @@ def bench_kv(nv, workloads, iters):
         return round(gbps, 1), round(gbps / HBM_PEAK_GBPS, 4)
 
     r2, r1, rd = rate(bytes_q, t2), rate(bytes_q, t1), rate(bytes_dq, tdq)
+    del sets
+    torch.cuda.empty_cache()
+    win = bench_kv_window(nv, iters)
     return {
         "workload": f"K/V bf16 [{heads},{tokens},{d}], 16-blocks along head_dim, four-over-six",
         "quantize_ms_per_tensor": round(t2, 5), "quantize_GBps": r2[0], "quantize_frac_hbm": r2[1],
@@ -196,7 +199,58 @@ def bench_kv(nv, workloads, iters):
         "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
         "note": "GB/s = algorithmic bytes / event time per call; quantize = amax pass inside the call, "
                 "quantize_1pass = amax supplied by the producing GEMM's epilogue",
+        "window": win,
     }
+
+
+def bench_kv_window(nv, iters):
+    """Consumer side at the pages' inference configuration: 8-frame chunks of
+    880 tokens x 24 heads x 128, keys smoothed and quantized per chunk; the
+    attention window of the chunk at frame 64 (global sink frames 0-7, shot
+    sink frames 16-23, the 32 frames before) rebuilt in one launch each for K
+    and V."""
+    import torch
+    chunk_frames, frame_rows, d = 8, 880 * 24, 128
+    rows = chunk_frames * frame_rows
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    kc, vc = [], []
+    wsz = nv.lib.nvfp4_kv_smooth_workspace_size(rows, d)
+    ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    for c in range(8):
+        k = (torch.randn((rows, d), generator=g, device="cuda") + 2.0).to(torch.bfloat16)
+        v = torch.randn((rows, d), generator=g, device="cuda").to(torch.bfloat16)
+        kc.append(nv.kv_quantize_smoothed(k, workspace=ws))
+        vc.append(nv.kv_quantize(v, "4over6"))
+    torch.cuda.synchronize()
+
+    def smooth(i):
+        nv.kv_quantize_smoothed(k, out=kc[7][0], means=kc[7][1], workspace=ws)
+
+    t_smooth = time_events(smooth, iters)
+    runs = nv.kv_window_plan(64, chunk_frames, 32, 8, 16, 8)
+    kparts = [(kc[c][0], kc[c][1], f0 * frame_rows, n * frame_rows) for c, f0, n in runs]
+    vparts = [(vc[c], None, f0 * frame_rows, n * frame_rows) for c, f0, n in runs]
+    wrows = sum(p[3] for p in kparts)
+    kout = torch.empty((wrows, d), dtype=torch.bfloat16, device="cuda")
+    vout = torch.empty((wrows, d), dtype=torch.bfloat16, device="cuda")
+
+    def window(i):
+        nv.kv_dequantize_window(kparts, out=kout)
+        nv.kv_dequantize_window(vparts, out=vout)
+
+    t_win = time_events(window, iters)
+    n = wrows * d
+    bytes_win = 2 * (n * 9 / 16 + n * 2) + wrows * 4          # K and V: packed in, bf16 out; K means
+    bytes_smooth = rows * d * (2 + 2 + 9 / 16) + rows * 4      # two reads of the keys, packed out, means
+    gbps = bytes_win / (t_win * 1e-3) / 1e9
+    gbs = bytes_smooth / (t_smooth * 1e-3) / 1e9
+    return {"workload": f"window of the chunk at frame 64: {len(runs)} chunks x {rows} rows x {d}, K and V",
+            "frames": wrows // frame_rows, "window_ms_k_and_v": round(t_win, 5), "window_GBps": round(gbps, 1),
+            "window_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "smoothed_k_quantize_ms_per_chunk": round(t_smooth, 5),
+            "smoothed_k_quantize_GBps": round(gbs, 1),
+            "note": "window GB/s = (packed K and V + K means read, bf16 K and V written) / time of the two launches; "
+                    "smoothed quantize bytes count both reads of the chunk"}
 
 
 def bench_extra(nv, workloads, iters):

@@ -257,6 +257,67 @@ nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scale
                                       int64_t rows, int64_t cols, uint8_t *codes_t, uint8_t *scales_t,
                                       float *alpha_t, hipStream_t stream);
 
+/* ------------------------------------------------ KV cache, consumer side */
+
+/* Workspace of nvfp4_kv_quantize_smoothed (amax partials), at most 4 KiB. */
+size_t nvfp4_kv_smooth_workspace_size(int64_t vectors, int64_t head_dim);
+
+/*
+ * nvfp4_kv_quantize_smoothed -- key smoothing, then the KV quantizer: every
+ * key vector (head_dim elements, a power of two in [16, 1024]) loses its mean
+ * over head_dim, and the smoothed keys are quantized as nvfp4_kv_quantize
+ * does (16-blocks along head_dim, one alpha for the tensor -- call it once
+ * per chunk for the per-chunk global scale).  means [vectors] (fp32, device)
+ * receives each vector's mean, which nvfp4_kv_dequantize_window adds back.
+ * fp32 order: per 16-element block a partial sum in index order, the
+ * partials added in block order, mean = sum / head_dim, key - mean.
+ * k: [vectors][head_dim] contiguous, 16-byte aligned; workspace >=
+ * nvfp4_kv_smooth_workspace_size().
+ * Source: "Key smoothing" (subtract the mean over the head dimension from
+ * each key vector) and "Chunkwise quantization procedure" (per-chunk,
+ * per-layer global scale), NVFP4 Inference section of the architecture
+ * walkthrough page.  Keeping the means for the add-back is this library's
+ * reading: without it each key's scores with a query change by mean * sum(q).
+ */
+nvfp4_status_t nvfp4_kv_quantize_smoothed(const void *k, int k_dtype, int64_t vectors, int64_t head_dim, int rule,
+                                          uint8_t *codes, uint8_t *scales, float *alpha, float *means,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One cached chunk's contribution to an attention window: rows
+ * [first, first + count) of a chunk quantized by nvfp4_kv_quantize (means
+ * NULL) or nvfp4_kv_quantize_smoothed (means = its means array).  codes
+ * [chunk rows][head_dim/2], scales [chunk rows][head_dim/16], alpha: device
+ * pointers as the quantizer wrote them (codes and scales 16-byte aligned). */
+typedef struct {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *alpha;
+    const float *means;
+    int64_t first;
+    int64_t count;
+} nvfp4_kv_segment_t;
+
+#define NVFP4_MAX_KV_SEGMENTS 32
+
+/*
+ * nvfp4_kv_dequantize_window -- rebuild an attention window from cached
+ * chunks in ONE launch: the segments' rows, dequantized ((q * s) * alpha,
+ * plus the vector's mean for smoothed keys, one fp32 add), written one after
+ * another into out [sum of counts][head_dim] (row stride ldo elements, fp32 or
+ * bf16 = round-to-nearest-even, 16-byte aligned rows).  segments: a HOST
+ * array of n_segments <= NVFP4_MAX_KV_SEGMENTS entries, read during the call
+ * (it can be reused as soon as the call returns).  The caller plans the
+ * segments: global sink, shot sink and the sliding window of recent chunks,
+ * with overlapping frames listed once.
+ * Source: "Parallel CUDA dequantization kernel" (chunks of the active window
+ * reconstructed together into the window buffer in one launch) and the
+ * effective key/value set (global sink, shot-level sink, sliding window,
+ * duplicates removed) of the Multi-Shot Attention Sink section of the
+ * architecture walkthrough page.
+ */
+nvfp4_status_t nvfp4_kv_dequantize_window(const nvfp4_kv_segment_t *segments, int n_segments, int64_t head_dim,
+                                          void *out, int out_dtype, int64_t ldo, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,6 +38,15 @@ class NVFP4Error(RuntimeError):
         self.status = status
 
 
+class KvSegment(ctypes.Structure):
+    """nvfp4_kv_segment_t"""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+                ("means", ctypes.c_void_p), ("first", ctypes.c_int64), ("count", ctypes.c_int64)]
+
+
+MAX_KV_SEGMENTS = 32
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python nvfp4_w4a4_quantized_04_amd/build.py` "
@@ -65,6 +74,12 @@ def _load():
     L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_wgrad.restype = i32
     L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, i32, P, i32, i64, P, sz, P]
+    L.nvfp4_kv_smooth_workspace_size.restype = sz
+    L.nvfp4_kv_smooth_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_kv_quantize_smoothed.restype = i32
+    L.nvfp4_kv_quantize_smoothed.argtypes = [P, i32, i64, i64, i32, P, P, P, P, P, sz, P]
+    L.nvfp4_kv_dequantize_window.restype = i32
+    L.nvfp4_kv_dequantize_window.argtypes = [ctypes.POINTER(KvSegment), i32, i64, P, i32, i64, P]
     L.nvfp4_quantize_col16_rht.restype = i32
     L.nvfp4_quantize_col16_rht.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_transpose_tile16.restype = i32
@@ -77,7 +92,8 @@ lib = _load()
 EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
-            "nvfp4_quantize_col16_rht"]
+            "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",
+            "nvfp4_kv_dequantize_window"]
 
 
 def _check(fn: str, st: int):
@@ -316,3 +332,79 @@ def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.T
         _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
     return out
+
+
+def kv_quantize_smoothed(k: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
+                         means: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Key smoothing (each key vector minus its mean over head_dim), then the
+    KV quantizer; returns (packed keys, fp32 means [vectors])."""
+    _need_gpu(k)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    d = k.shape[-1]
+    v = k.numel() // d
+    if out is None:
+        out = empty_packed(v, d, ROW16, k.device)
+    if means is None:
+        means = torch.empty(v, dtype=torch.float32, device=k.device)
+    if workspace is None:
+        workspace = torch.empty(lib.nvfp4_kv_smooth_workspace_size(v, d), dtype=torch.uint8, device=k.device)
+    _check("nvfp4_kv_quantize_smoothed", lib.nvfp4_kv_quantize_smoothed(
+        _ptr(k), _dtype_code(k), v, d, _rule(rule), _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha),
+        _ptr(means), _ptr(workspace), workspace.numel(), _stream()))
+    return out, means
+
+
+def kv_dequantize_window(parts, out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rebuild an attention window in one launch.  parts: sequence of
+    (packed chunk, means or None, first row, row count); rows are written in
+    that order."""
+    parts = list(parts)
+    if len(parts) > MAX_KV_SEGMENTS:
+        raise ValueError(f"at most {MAX_KV_SEGMENTS} segments")
+    if not parts:
+        raise ValueError("no segments")
+    d = parts[0][0].cols
+    rows = sum(int(c) for _, _, _, c in parts)
+    segs = (KvSegment * len(parts))()
+    for i, (t, means, first, count) in enumerate(parts):
+        if t.block != ROW16 or t.cols != d:
+            raise ValueError("segments must be ROW16 chunks of one head_dim")
+        if first < 0 or count < 0 or first + count > t.rows:
+            raise ValueError("segment rows out of range")
+        _need_gpu(t.codes, means)
+        segs[i] = KvSegment(_ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), _ptr(means), int(first), int(count))
+    if out is None:
+        out = torch.empty((rows, d), dtype=out_dtype, device=parts[0][0].codes.device)
+    _check("nvfp4_kv_dequantize_window", lib.nvfp4_kv_dequantize_window(
+        segs, len(parts), d, _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
+    return out
+
+
+def kv_window_plan(frame: int, chunk_frames: int, window_frames: int, global_sink_frames: int = 0,
+                   shot_start: int | None = None, shot_frames: int = 0):
+    """Frames the attention of the chunk starting at `frame` reads, as
+    (chunk index, first frame inside the chunk, frame count) runs in frame
+    order: the global sink (frames [0, global_sink_frames)), the shot sink
+    (frames [shot_start, shot_start + shot_frames)) and the sliding window
+    (the window_frames frames before `frame`), each frame once.  Only frames
+    before `frame` exist in the cache."""
+    ranges = [(max(0, frame - window_frames), frame), (0, min(global_sink_frames, frame))]
+    if shot_start is not None and shot_frames > 0:
+        ranges.append((shot_start, min(shot_start + shot_frames, frame)))
+    ranges = sorted((a, b) for a, b in ranges if b > a)
+    merged = []
+    for a, b in ranges:
+        if merged and a <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], b))
+        else:
+            merged.append((a, b))
+    runs = []
+    for a, b in merged:
+        f = a
+        while f < b:
+            c = f // chunk_frames
+            e = min(b, (c + 1) * chunk_frames)
+            runs.append((c, f - c * chunk_frames, e - f))
+            f = e
+    return runs

@@ -313,4 +313,72 @@ nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows
                        (float *)workspace, stream, rht_signs);
 }
 
+size_t nvfp4_kv_smooth_workspace_size(int64_t vectors, int64_t head_dim)
+{
+    (void)vectors; (void)head_dim;
+    return kAmaxBytes;
+}
+
+nvfp4_status_t nvfp4_kv_quantize_smoothed(const void *k, int k_dtype, int64_t vectors, int64_t head_dim, int rule,
+                                          uint8_t *codes, uint8_t *scales, float *alpha, float *means,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!dtype_ok(k_dtype) || !rule_ok(rule))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(vectors, head_dim) || head_dim < 16 || head_dim > 1024 || (head_dim & (head_dim - 1)) != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!alpha || (vectors > 0 && (!k || !codes || !scales || !means)))
+        return NVFP4_ERR_NULL;
+    if ((k && !aligned16(k)) || (codes && !aligned16(codes)) || (scales && !aligned16(scales)) ||
+        (means && ((uintptr_t)means & 3u)) || ((uintptr_t)alpha & 3u))
+        return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_kv_smooth_workspace_size(vectors, head_dim))
+        return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return NVFP4_ERR_ALIGN;
+    return launch_status(launch_kv_smooth_quantize(k, k_dtype, vectors, head_dim, rule, codes, scales, alpha, means,
+                                                   (float *)workspace, stream));
+}
+
+nvfp4_status_t nvfp4_kv_dequantize_window(const nvfp4_kv_segment_t *segments, int n_segments, int64_t head_dim,
+                                          void *out, int out_dtype, int64_t ldo, hipStream_t stream)
+{
+    if (!dtype_ok(out_dtype))
+        return NVFP4_ERR_DTYPE;
+    if (n_segments < 0 || n_segments > NVFP4_MAX_KV_SEGMENTS || head_dim < 16 || head_dim % 16 != 0 ||
+        head_dim >= kMaxDim || ldo < head_dim)
+        return NVFP4_ERR_SHAPE;
+    if (n_segments > 0 && !segments)
+        return NVFP4_ERR_NULL;
+    static_assert(NVFP4_MAX_KV_SEGMENTS == kMaxKvSegments, "segment table size");
+    KvWindowArgs a{};
+    a.n = n_segments;
+    a.bpr = (int)(head_dim / 16);
+    int64_t rows = 0, wgs = 0;
+    for (int i = 0; i < n_segments; i++) {
+        const nvfp4_kv_segment_t &g = segments[i];
+        if (g.first < 0 || g.count < 0 || g.first >= kMaxDim || g.count >= kMaxDim)
+            return NVFP4_ERR_SHAPE;
+        if (g.count > 0 && (!g.codes || !g.scales || !g.alpha))
+            return NVFP4_ERR_NULL;
+        if ((g.codes && !aligned16(g.codes)) || (g.scales && !aligned16(g.scales)) || ((uintptr_t)g.alpha & 3u) ||
+            ((uintptr_t)g.means & 3u))
+            return NVFP4_ERR_ALIGN;
+        if (g.count * a.bpr >= kMaxDim)
+            return NVFP4_ERR_SHAPE;
+        a.seg[i] = KvSegmentDev{g.codes, g.scales, g.alpha, g.means, g.first, g.count, rows, wgs};
+        rows += g.count;
+        wgs += (g.count * a.bpr + kQuantThreads - 1) / kQuantThreads;
+    }
+    a.wgs = wgs;
+    if (rows >= kMaxDim || rows * a.bpr >= kMaxDim)
+        return NVFP4_ERR_SHAPE;
+    a.rows = rows;
+    if (rows > 0 && !out)
+        return NVFP4_ERR_NULL;
+    if (out && (!aligned16(out) || (ldo * (out_dtype == NVFP4_BF16 ? 2 : 4)) % 16 != 0))
+        return NVFP4_ERR_ALIGN;
+    return launch_status(launch_kv_window(a, out, out_dtype, ldo, stream));
+}
+
 }  // extern "C"

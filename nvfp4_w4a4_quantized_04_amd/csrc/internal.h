@@ -35,6 +35,33 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
                              int64_t cols, int block, void *y, int ydtype, int64_t ldy, hipStream_t s);
 
+// Key smoothing + quantization of a [vectors][head_dim] key tensor (two passes:
+// means and amax, then quantize); head_dim a power of two in [16, 1024].
+hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, int64_t head_dim, int rule,
+                                     uint8_t *codes, uint8_t *scales, float *alpha, float *means, float *partials,
+                                     hipStream_t s);
+
+// Window reconstruction from cached chunks (segment table passed by value).
+constexpr int kMaxKvSegments = 32;
+struct KvSegmentDev {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *alpha;
+    const float *means;     // NULL: no mean to add back
+    int64_t first;          // first row (vector) of the chunk taken
+    int64_t count;          // rows taken
+    int64_t out_row;        // first output row of this segment
+    int64_t wg0;            // first workgroup serving this segment
+};
+struct KvWindowArgs {
+    KvSegmentDev seg[kMaxKvSegments];
+    int n;
+    int bpr;                // 16-element blocks per row (head_dim / 16)
+    int64_t rows;           // output rows in total
+    int64_t wgs;            // workgroups in total
+};
+hipError_t launch_kv_window(const KvWindowArgs &a, void *y, int ydtype, int64_t ldy, hipStream_t s);
+
 struct GemmOperand {
     const uint8_t *codes;
     const uint8_t *scales;

@@ -432,7 +432,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_rows(const uint8_t *_
     if (b >= rows * bpr)
         return;
     const float alpha = *alpha_p;
-    const int64_t r = b / bpr;
+    // 32-bit division while the block index fits (every tensor here does)
+    const int64_t r = b < 0x7fffffff ? (int64_t)((uint32_t)b / (uint32_t)bpr) : b / bpr;
     const int64_t cb = b - r * bpr;
     const uint2 c = *reinterpret_cast<const uint2 *>(codes + b * 8);
     const int64_t soff = TILE ? (r / 16) * bpr + cb : b;
@@ -477,6 +478,150 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_col16(const uint8_t *
 #pragma unroll
     for (int i = 0; i < 16; i++)
         store1<O>(y + (rb * 16 + i) * ldy + c, v[i]);
+}
+
+// ------------------------------------------------ KV cache: key smoothing
+
+// Key smoothing ("Key smoothing", NVFP4 Inference section of the architecture
+// walkthrough page): each key vector of d = head_dim elements loses its mean
+// over d.  fp32 order (shared with the quantize pass below): each 16-element
+// block's partial sum in index order, the d/16 partials added in block order,
+// mean = sum / d, key[u] - mean.  G = d/16 lanes hold one vector (one block
+// each); the partials travel by shuffles, so every lane of the group forms the
+// same sum in the same order.
+template <typename T>
+__global__ __launch_bounds__(kAmaxThreads) void k_kv_smooth_amax(const T *__restrict__ x, int64_t vectors, int g_log2,
+                                                                 float *__restrict__ means,
+                                                                 float *__restrict__ partials)
+{
+    __shared__ float red[kAmaxThreads / 64];
+    const int G = 1 << g_log2;
+    const int64_t d = (int64_t)G * 16;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & (G - 1), base = lane - j;
+    float a = 0.0f;
+    const int64_t per_iter = ((int64_t)gridDim.x * kAmaxThreads) >> g_log2;
+    for (int64_t v = (((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) >> g_log2); v < vectors; v += per_iter) {
+        float f[16];
+        load16(x + v * d + j * 16, f);
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            p = p + f[i];
+        float sum = 0.0f;
+        for (int b = 0; b < G; b++)
+            sum = sum + __shfl(p, base + b, 64);
+        const float mean = sum / (float)d;
+        if (j == 0)
+            means[v] = mean;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            a = fmaxf(a, fabsf(f[i] - mean));
+    }
+    a = wave_max(a);
+    if (lane == 0)
+        red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+#pragma unroll
+        for (int w = 1; w < kAmaxThreads / 64; w++)
+            b = fmaxf(b, red[w]);
+        partials[blockIdx.x] = b;
+    }
+}
+
+// Quantize the smoothed keys: one lane per 16-element block, the vector's mean
+// (written by the pass above) subtracted first.
+template <typename T, bool RULE4>
+__global__ __launch_bounds__(kQuantThreads) void k_kv_quant_smoothed(const T *__restrict__ x, int64_t vectors, int g_log2,
+                                                                     const float *__restrict__ means,
+                                                                     const float *__restrict__ amax_src, int n_amax,
+                                                                     uint8_t *__restrict__ codes,
+                                                                     uint8_t *__restrict__ scales,
+                                                                     float *__restrict__ alpha_out)
+{
+    __shared__ float ktab[128];
+    const int64_t nb = vectors << g_log2;
+    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    float f[16];
+    float mean = 0.0f;
+    if (b < nb) {
+        load16(x + b * 16, f);
+        mean = means[b >> g_log2];
+    }
+    const float alpha = block_alpha(amax_src, n_amax);
+    build_kappa_table(ktab, alpha);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *alpha_out = alpha;
+    if (b >= nb)
+        return;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        f[i] = f[i] - mean;
+    uint32_t c0, c1, sb;
+    quant_block16<RULE4>(f, alpha, ktab, c0, c1, sb);
+    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
+    scales[b] = (uint8_t)sb;
+}
+
+// ------------------------------------------------ KV cache: window dequantize
+
+// One launch reconstructs the attention window from several cached chunks
+// ("Parallel CUDA dequantization kernel" paragraph: chunks of the active window
+// dequantized together into the window buffer): segment i contributes rows
+// [first, first + count) of its chunk, in segment order.  One lane per 16
+// elements; the vector's mean is added back for smoothed keys.
+// Store 16 fp32 values as fp32 or bf16 (round to nearest even).
+template <typename O>
+__device__ __forceinline__ void store16(O *out, const float (&v)[16])
+{
+    if (sizeof(O) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            reinterpret_cast<float4 *>(out)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __bf16 lo = (__bf16)v[2 * i], hi = (__bf16)v[2 * i + 1];
+            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        reinterpret_cast<uint4 *>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+// Each workgroup serves one segment (the host gives segment i the workgroups
+// [wg0_i, wg0_{i+1})), so the segment's pointers are uniform; one lane per
+// 16-element block of the segment's rows.
+template <typename O>
+__global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *__restrict__ y, int64_t ldy)
+{
+    const int wg = blockIdx.x;
+    int si = 0;
+    while (si + 1 < a.n && wg >= a.seg[si + 1].wg0)
+        si++;
+    const KvSegmentDev &sg = a.seg[si];
+    const uint32_t bpr = (uint32_t)a.bpr;
+    // count * bpr < 2^31 (checked by the caller): 32-bit index arithmetic
+    const uint32_t local = (uint32_t)(wg - sg.wg0) * kQuantThreads + threadIdx.x;
+    if (local >= (uint32_t)sg.count * bpr)
+        return;
+    const uint32_t r = local / bpr;
+    const int cb = (int)(local - r * bpr);
+    const int64_t v = sg.first + r;
+    const int64_t blk = v * bpr + cb;
+    const uint2 c = *reinterpret_cast<const uint2 *>(sg.codes + blk * 8);
+    float val[16];
+    decode16(c.x, c.y, e4m3_get<0>(sg.scales[blk]), *sg.alpha, val);
+    if (sg.means) {
+        const float m = sg.means[v];
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            val[i] = val[i] + m;
+    }
+    store16(y + (sg.out_row + r) * ldy + cb * 16, val);
 }
 
 // ------------------------------------------------------------ launchers
@@ -599,5 +744,44 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const 
     }
     return hipGetLastError();
 }
+
+hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, int64_t head_dim, int rule,
+                                     uint8_t *codes, uint8_t *scales, float *alpha, float *means, float *partials,
+                                     hipStream_t s)
+{
+    int g_log2 = 0;
+    while ((16 << g_log2) < head_dim)
+        g_log2++;
+    const int n = amax_partials(vectors, head_dim);
+    if (dtype == 1)
+        k_kv_smooth_amax<uint16_t><<<n, kAmaxThreads, 0, s>>>((const uint16_t *)x, vectors, g_log2, means, partials);
+    else
+        k_kv_smooth_amax<float><<<n, kAmaxThreads, 0, s>>>((const float *)x, vectors, g_log2, means, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t nb = vectors << g_log2;
+    const unsigned grid = (unsigned)(nb > 0 ? (nb + kQuantThreads - 1) / kQuantThreads : 1);
+    if (dtype == 1) {
+        if (rule) k_kv_quant_smoothed<uint16_t, true><<<grid, kQuantThreads, 0, s>>>((const uint16_t *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
+        else      k_kv_quant_smoothed<uint16_t, false><<<grid, kQuantThreads, 0, s>>>((const uint16_t *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
+    } else {
+        if (rule) k_kv_quant_smoothed<float, true><<<grid, kQuantThreads, 0, s>>>((const float *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
+        else      k_kv_quant_smoothed<float, false><<<grid, kQuantThreads, 0, s>>>((const float *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_window(const KvWindowArgs &a, void *y, int ydtype, int64_t ldy, hipStream_t s)
+{
+    if (a.wgs == 0)
+        return hipSuccess;
+    if (ydtype == 1)
+        k_kv_window<uint16_t><<<(unsigned)a.wgs, kQuantThreads, 0, s>>>(a, (uint16_t *)y, ldy);
+    else
+        k_kv_window<float><<<(unsigned)a.wgs, kQuantThreads, 0, s>>>(a, (float *)y, ldy);
+    return hipGetLastError();
+}
+
 
 }  // namespace nvfp4

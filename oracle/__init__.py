@@ -81,6 +81,8 @@ def lib():
         L.nvo_rht16.restype = None
         L.nvo_quantize_col16_rht.argtypes = [P, i64, i64, i64, ctypes.c_int, ctypes.c_uint, P, P, P, P, P]
         L.nvo_quantize_col16_rht.restype = None
+        L.nvo_kv_smooth.argtypes = [P, i64, i64, P, P]
+        L.nvo_kv_smooth.restype = None
         L.nvo_dequantize.argtypes = [P, P, ctypes.c_float, i64, i64, ctypes.c_int, P, i64]
         L.nvo_dequantize.restype = None
         L.nvo_gemm_f64.argtypes = [P, P, ctypes.c_float, ctypes.c_int, P, P, ctypes.c_float,
@@ -246,6 +248,37 @@ def gemm_f64_sampled(a: Packed, b: Packed, ms: np.ndarray, ns: np.ndarray) -> np
                                _ptr(np.ascontiguousarray(cb)), _ptr(np.ascontiguousarray(sb)), float(ab), b2,
                                K, _ptr(ms), _ptr(ns), ms.size, _ptr(out))
     return out
+
+
+def kv_smooth(k: np.ndarray):
+    """Key smoothing of [vectors, d] keys: (smoothed keys fp32, means fp32)."""
+    x = _as_f32(k)
+    v, d = x.shape
+    out = np.empty_like(x)
+    means = np.empty(v, np.float32)
+    lib().nvo_kv_smooth(_ptr(x), v, d, _ptr(out), _ptr(means))
+    return out, means
+
+
+def kv_quantize_smoothed(k: np.ndarray, rule: int = FOUR_OVER_SIX):
+    """Smoothed keys quantized in 16-blocks along head_dim, one alpha: (Packed, means)."""
+    ks, means = kv_smooth(k)
+    return quantize(ks, ROW16, rule), means
+
+
+def kv_window(parts, out_bf16: bool = True) -> np.ndarray:
+    """The attention window the consumer reconstructs: for each part (Packed
+    chunk, means or None, first vector, vector count) the dequantized rows
+    [first, first + count), plus the chunk's means when given (one fp32 add),
+    concatenated in order; bf16 (round to nearest even) or fp32."""
+    rows = []
+    for p, means, first, count in parts:
+        y = dequantize(p)[first:first + count]
+        if means is not None:
+            y = (y + means[first:first + count, None].astype(np.float32)).astype(np.float32)
+        rows.append(y)
+    y = np.concatenate(rows, axis=0) if rows else np.zeros((0, 0), np.float32)
+    return bf16_rne(y) if out_bf16 else y
 
 
 def transpose_tile16(p: Packed) -> Packed:

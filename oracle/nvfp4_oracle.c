@@ -365,6 +365,36 @@ void nvo_quantize_col16_rht(const float *x, int64_t rows, int64_t cols, int64_t 
     free(t);
 }
 
+/* ------------------------------------------------------------ K smoothing */
+
+/* Key smoothing before KV quantization (architecture walkthrough page, NVFP4
+ * Inference section, "Key smoothing"): every key vector loses its mean over
+ * the head dimension, K'[u] = K[u] - (1/d) sum_u K[u].
+ *
+ * Reading of the fp32 order: partial sums of each 16-element block in index
+ * order, the d/16 partials added in block order, mean = RN32(sum / d),
+ * K'[u] = RN32(K[u] - mean).  The means are returned so the consumer can add
+ * them back (the pages do not say what happens to them; without the add-back
+ * a key's dot products with a query change by mean * sum(q)). */
+void nvo_kv_smooth(const float *x, int64_t vectors, int64_t d, float *out, float *means)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < vectors; v++) {
+        const float *k = x + v * d;
+        float s = 0.0f;
+        for (int64_t b = 0; b < d / 16; b++) {
+            float p = 0.0f;
+            for (int i = 0; i < 16; i++)
+                p = p + k[b * 16 + i];
+            s = s + p;
+        }
+        const float m = s / (float)d;
+        means[v] = m;
+        for (int64_t u = 0; u < d; u++)
+            out[v * d + u] = k[u] - m;
+    }
+}
+
 /* Dequantize to fp32 y [rows][cols] (original orientation, row stride ldy):
  * xhat = RN32(RN32(q * s) * alpha). */
 void nvo_dequantize(const uint8_t *codes, const uint8_t *scales, float alpha, int64_t rows,

@@ -116,6 +116,26 @@ def test_hip_build_script_loads_without_the_library():
     assert {"api.hip", "gemm.hip", "quant.hip", "pack.hip"} <= set(names)
 
 
+def test_kv_consumer_validation_without_gpu():
+    import nvfp4_w4a4_quantized_04_amd as m
+    q = m.lib.nvfp4_kv_quantize_smoothed
+    assert q(FAKE, 1, 10, 96, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2        # head_dim not a power of two
+    assert q(FAKE, 1, 10, 128, 1, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == 1       # means
+    assert q(FAKE, 1, 10, 128, 1, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 5          # workspace
+    w = m.lib.nvfp4_kv_dequantize_window
+    seg = (m.KvSegment * 33)()
+    for i in range(33):
+        seg[i] = m.KvSegment(FAKE, FAKE, FAKE, None, 0, 4)
+    assert w(seg, 33, 128, FAKE, 1, 128, None) == 2                   # too many segments
+    assert w(seg, 2, 120, FAKE, 1, 128, None) == 2                    # head_dim % 16
+    assert w(seg, 2, 128, FAKE, 1, 100, None) == 2                    # ldo < head_dim
+    assert w(seg, 2, 128, FAKE + 8, 1, 128, None) == 3                # output alignment
+    bad = (m.KvSegment * 2)(m.KvSegment(FAKE, FAKE, FAKE, None, 0, 4), m.KvSegment(None, FAKE, FAKE, None, 0, 4))
+    assert w(bad, 2, 128, FAKE, 1, 128, None) == 1                    # codes NULL
+    neg = (m.KvSegment * 1)(m.KvSegment(FAKE, FAKE, FAKE, None, -1, 4))
+    assert w(neg, 1, 128, FAKE, 1, 128, None) == 2
+
+
 def test_no_cpu_fallback():
     import torch
     import nvfp4_w4a4_quantized_04_amd as m

@@ -459,3 +459,38 @@ def test_rht_wgrad_product_unchanged_before_quantization():
     got = rot(dy).T @ rot(x)
     want = dy.astype(np.float64).T @ x.astype(np.float64)
     assert np.max(np.abs(got - want)) <= 1e-5 * np.max(np.abs(want))
+
+
+def test_kv_smooth_closed_forms():
+    # integer keys: every partial sum is exact, so the mean is the exact mean
+    # rounded once, and a constant offset added to a vector leaves the smoothed
+    # vector unchanged when the mean stays exact
+    rng = np.random.default_rng(40)
+    k = rng.integers(-200, 200, (32, 128)).astype(np.float32)
+    k[:, 0] += (128 * 7 - k.sum(axis=1))            # make every sum 896 = 7 * 128: mean exactly 7
+    ks, m = oracle.kv_smooth(k)
+    assert np.all(m == np.float32(7.0))
+    assert np.array_equal(ks, k - np.float32(7.0))
+    ks2, m2 = oracle.kv_smooth(k + np.float32(64.0))
+    assert np.all(m2 == np.float32(71.0)) and np.array_equal(ks2, ks)
+    # a constant vector smooths to exact zeros; a zero-mean vector is unchanged
+    c = np.full((2, 64), 3.25, np.float32)
+    assert not np.any(oracle.kv_smooth(c)[0])
+    z = np.tile(np.array([1.0, -1.0], np.float32), (3, 32))
+    zs, zm = oracle.kv_smooth(z)
+    assert np.all(zm == 0) and np.array_equal(zs, z)
+
+
+def test_kv_smooth_order_and_quantize():
+    # random keys: the mean is within a few ulps of the fp64 mean, the
+    # smoothed keys are the one-rounding differences, and the packed result is
+    # the plain quantizer applied to them
+    rng = np.random.default_rng(41)
+    k = (rng.standard_normal((64, 128)) * 3 + rng.standard_normal((64, 1)) * 10).astype(np.float32)
+    ks, m = oracle.kv_smooth(k)
+    exact = k.astype(np.float64).mean(axis=1)
+    assert np.all(np.abs(m - exact) <= 1e-5 * np.abs(k).sum(axis=1) / 128)
+    assert np.array_equal(ks, (k - m[:, None]).astype(np.float32))
+    p, m2 = oracle.kv_quantize_smoothed(k)
+    q = oracle.quantize(ks, ROW16, FOUR_OVER_SIX)
+    assert np.array_equal(p.codes, q.codes) and np.array_equal(p.scales, q.scales) and np.array_equal(m, m2)
