@@ -281,6 +281,55 @@ def kv_window(parts, out_bf16: bool = True) -> np.ndarray:
     return bf16_rne(y) if out_bf16 else y
 
 
+def lora_down_bf16(x: np.ndarray, lora_a: np.ndarray) -> np.ndarray:
+    """U = x A^T of the LoRA branch, rounded to bf16 (uint16 bits): x [m, k]
+    and lora_a [r, k] as bf16 bits (or float32), the dot products summed in
+    fp64 (every product of two bf16 values is exact) and rounded once."""
+    xf = _bf16_or_f32(x).astype(np.float64)
+    af = _bf16_or_f32(lora_a).astype(np.float64)
+    return _bf16_rne_f64(xf @ af.T)
+
+
+def linear_lora_f64(a: Packed, w: Packed, u_bf16: np.ndarray, lora_b: np.ndarray, scale: float) -> np.ndarray:
+    """The W4A4 linear with a BF16 LoRA branch, in fp64: the NVFP4 product
+    (gemm_f64) plus scale * U B^T, U [m, r] and lora_b [n, r] bf16 bits."""
+    base = gemm_f64(a, w)
+    u = _bf16_or_f32(u_bf16).astype(np.float64)
+    b = _bf16_or_f32(lora_b).astype(np.float64)
+    return base + float(scale) * (u @ b.T)
+
+
+def _bf16_or_f32(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x.astype(np.float32)
+
+
+def _bf16_rne_f64(y: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even) in one step: the
+    exact bf16 neighbours of each value are compared in fp64."""
+    y = np.asarray(y, np.float64)
+    f = y.astype(np.float32)                       # may round; corrected below
+    bits = f.view(np.uint32).astype(np.int64)
+    lo = (bits & ~0xFFFF) & 0xFFFFFFFF             # bf16 truncation of f (toward zero in magnitude)
+    cand = []
+    for d in (-0x10000, 0, 0x10000, 0x20000):
+        c = (lo + d) & 0xFFFFFFFF
+        cand.append(c)
+    cand = np.stack(cand)
+    vals = cand.astype(np.uint32).view(np.float32).astype(np.float64)
+    err = np.abs(vals - y[None])
+    best = np.argmin(err, axis=0)
+    # ties: prefer the candidate with an even bf16 mantissa
+    out = np.take_along_axis(cand, best[None], axis=0)[0]
+    e_best = np.take_along_axis(err, best[None], axis=0)[0]
+    for k in range(4):
+        tie = (err[k] == e_best) & (((cand[k] >> 16) & 1) == 0) & (cand[k] != out)
+        out = np.where(tie, cand[k], out)
+    return (out >> 16).astype(np.uint16)
+
+
 def transpose_tile16(p: Packed) -> Packed:
     """W^T of a TILE16-packed W, element by element: element (i, j) of W is
     element (j, i) of W^T, each 16x16 tile keeps its scale byte and the tensor

@@ -132,3 +132,55 @@ def test_sampled_matches_full():
     ms = np.array([0, 5, 63, 17], np.int64)
     ns = np.array([3, 63, 0, 17], np.int64)
     assert np.array_equal(oracle.gemm_f64_sampled(A, B, ms, ns), C[ms, ns])
+
+
+def _bf16_brute(y: float) -> int:
+    """Nearest bf16 (ties to even mantissa) of a double, by search."""
+    f = np.float32(y)
+    b = int(np.array([f]).view(np.uint32)[0]) & ~0xFFFF
+    best = None
+    for d in range(-3, 4):
+        c = (b + d * 0x10000) & 0xFFFFFFFF
+        v = float(np.array([c], np.uint32).view(np.float32)[0])
+        key = (abs(v - y), (c >> 16) & 1)
+        if best is None or key < best[0]:
+            best = (key, c >> 16)
+    return best[1]
+
+
+def test_bf16_rounding_of_doubles():
+    rng = np.random.default_rng(50)
+    y = rng.standard_normal(5000) * 10.0 ** rng.uniform(-6, 6, 5000)
+    y[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 1.0 + 2.0 ** -8 + 2.0 ** -40]   # ties, near tie
+    got = oracle._bf16_rne_f64(y)
+    assert list(got[:4]) == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
+    assert np.array_equal(got, np.array([_bf16_brute(v) for v in y], np.uint16))
+
+
+def test_lora_down_integer_closed_form():
+    # small integers: every dot product is exact, U is its bf16 rounding
+    rng = np.random.default_rng(51)
+    x = rng.integers(-8, 9, (20, 64)).astype(np.float32)
+    a = rng.integers(-8, 9, (16, 64)).astype(np.float32)
+    u = oracle.lora_down_bf16(x, a)
+    exact = x.astype(np.int64) @ a.astype(np.int64).T
+    assert np.array_equal(u, np.array([[_bf16_brute(float(v)) for v in row] for row in exact], np.uint16))
+
+
+def test_linear_lora_reduces_to_the_plain_gemm_and_adds_the_branch():
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((32, 64)).astype(np.float32)
+    w = (rng.standard_normal((48, 64)) * 0.02).astype(np.float32)
+    A = oracle.quantize(x, ROW16, FOUR_OVER_SIX)
+    W = oracle.quantize(w, TILE16, FOUR_OVER_SIX)
+    u = np.zeros((32, 8), np.uint16)
+    b = oracle._bf16_rne_f64(rng.standard_normal((48, 8)))
+    assert np.array_equal(oracle.linear_lora_f64(A, W, u, b, 1.0), oracle.gemm_f64(A, W))
+    # one-hot branch: U[i, j] = 1, B[n, j] = 2 -> adds scale * 2 at (i, n) only
+    u[5, 3] = 0x3F80
+    b1 = np.zeros((48, 8), np.uint16)
+    b1[7, 3] = 0x4000
+    diff = oracle.linear_lora_f64(A, W, u, b1, 0.5) - oracle.gemm_f64(A, W)
+    want = np.zeros((32, 48))
+    want[5, 7] = 1.0
+    assert np.array_equal(diff, want)
