@@ -265,6 +265,25 @@ def bench_extra(nv, workloads, iters):
         out[name] = {"ms": round(ms, 4), "TFLOPs": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)}
         del sets
         torch.cuda.empty_cache()
+    # the QKV projection with the rank-128 BF16 LoRA branch (alpha 128)
+    m, k, n, r = 2640, 3072, 9216, 128
+    sets = linear_sets(nv, workloads, m, k, n, 2, 40)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    la = (torch.randn((r, k), generator=g, device="cuda") / k ** 0.5).to(torch.bfloat16)
+    lb = (torch.randn((n, r), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    u = torch.empty((m, r), dtype=torch.bfloat16, device="cuda")
+
+    def lora_step(i):
+        x_, w_, y_, ws_ = sets[i % len(sets)]
+        nv.linear_lora(x_, w_, la, lb, 1.0, torch.bfloat16, out=y_, workspace=ws_, u=u)
+
+    ms = time_events(lora_step, iters)
+    out["qkv_lora_r128_m2640_k3072_n9216"] = {
+        "ms": round(ms, 4), "TFLOPs": round(2 * m * (n * k + k * r + n * r) / (ms * 1e-3) / 1e12, 1),
+        "note": "flops of the NVFP4 product plus both LoRA products"}
+    del sets
+    torch.cuda.empty_cache()
     # weight gradient dW = dY^T X over 32768 tokens
     t, n, k = 32768, 3072, 3072
     g = torch.Generator(device="cuda")

@@ -192,6 +192,27 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
                             void *y, int y_dtype, int64_t ldy, float *y_amax,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * nvfp4_linear_lora -- the W4A4 linear with a BF16 LoRA branch:
+ *     y = nvfp4_linear(x, w) + lora_scale * U B^T,   U = bf16(x A^T)
+ * x [m][k] bf16 (ld ldx, 16-byte aligned rows), lora_a A [rank][k] and
+ * lora_b B [n][rank] bf16 contiguous, rank in {32, 64, 96, 128}, lora_scale
+ * the adapter scale (alpha / rank).  lora_u: caller buffer [m][rank] bf16
+ * that receives U (x A^T with fp32 accumulation, rounded once to bf16, as a
+ * bf16 linear layer computes it).  The rank-r update runs on bf16 MFMA in the
+ * same GEMM launch after the NVFP4 contraction; fp32 accumulation.  Other
+ * arguments and the workspace as nvfp4_linear.
+ * Source: "LoRA parameterization" (W ~ Dequant(Q(W0)) + (alpha/r) B A, rank
+ * 128, alpha 128, BF16 adapters) and the NVFP4 Inference section (the
+ * adapters kept as a separate BF16 branch on the quantized backbone) of the
+ * architecture walkthrough page.
+ */
+nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,
+                                 const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                 int w_scale_layout, int64_t n, const void *lora_a, const void *lora_b, int rank,
+                                 float lora_scale, void *lora_u, void *y, int y_dtype, int64_t ldy, float *y_amax,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace of nvfp4_wgrad: both COL16-packed operands plus amax partials. */
 size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in);
 

@@ -80,6 +80,9 @@ def _load():
     L.nvfp4_kv_quantize_smoothed.argtypes = [P, i32, i64, i64, i32, P, P, P, P, P, sz, P]
     L.nvfp4_kv_dequantize_window.restype = i32
     L.nvfp4_kv_dequantize_window.argtypes = [ctypes.POINTER(KvSegment), i32, i64, P, i32, i64, P]
+    L.nvfp4_linear_lora.restype = i32
+    L.nvfp4_linear_lora.argtypes = [P, i64, i64, i64, i32, P, P, P, i32, i64, P, P, i32, ctypes.c_float, P, P, i32,
+                                    i64, P, P, sz, P]
     L.nvfp4_quantize_col16_rht.restype = i32
     L.nvfp4_quantize_col16_rht.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_transpose_tile16.restype = i32
@@ -93,7 +96,7 @@ EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspac
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
             "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",
-            "nvfp4_kv_dequantize_window"]
+            "nvfp4_kv_dequantize_window", "nvfp4_linear_lora"]
 
 
 def _check(fn: str, st: int):
@@ -408,3 +411,31 @@ def kv_window_plan(frame: int, chunk_frames: int, window_frames: int, global_sin
             runs.append((c, f - c * chunk_frames, e - f))
             f = e
     return runs
+
+
+def linear_lora(x: torch.Tensor, w: NVFP4Tensor, lora_a: torch.Tensor, lora_b: torch.Tensor, lora_scale: float,
+                out_dtype=torch.bfloat16, rule="4over6", out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, u: torch.Tensor | None = None, amax_out=None):
+    """W4A4 linear plus the BF16 LoRA branch: y = quantize(x) @ w^T +
+    lora_scale * bf16(x @ lora_a^T) @ lora_b^T.  Returns (y, U)."""
+    _need_gpu(x, lora_a, lora_b)
+    if x.dtype != torch.bfloat16 or lora_a.dtype != torch.bfloat16 or lora_b.dtype != torch.bfloat16:
+        raise TypeError("the LoRA path takes bf16 x, lora_a and lora_b")
+    if x.dim() != 2 or x.stride(1) != 1 or not lora_a.is_contiguous() or not lora_b.is_contiguous():
+        raise ValueError("x 2D with unit column stride; lora_a, lora_b contiguous")
+    cw, sw, aw, lw, n, kw = w.operand()
+    m, k = x.shape
+    r = lora_a.shape[0]
+    if k != kw or lora_a.shape[1] != k or tuple(lora_b.shape) != (n, r):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if u is None:
+        u = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = linear_workspace(m, k, x.device)
+    _check("nvfp4_linear_lora", lib.nvfp4_linear_lora(
+        _ptr(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n, _ptr(lora_a), _ptr(lora_b), r,
+        float(lora_scale), _ptr(u), _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return out, u

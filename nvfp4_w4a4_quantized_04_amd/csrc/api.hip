@@ -227,6 +227,55 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
     return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, y_amax, stream));
 }
 
+nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,
+                                 const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                 int w_scale_layout, int64_t n, const void *lora_a, const void *lora_b, int rank,
+                                 float lora_scale, void *lora_u, void *y, int y_dtype, int64_t ldy, float *y_amax,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    // the NVFP4 part is nvfp4_linear's; the branch adds its own checks
+    if (rank < 32 || rank > 128 || rank % 32 != 0 || !(lora_scale == lora_scale) || lora_scale == 0.0f ||
+        __builtin_isinf(lora_scale))
+        return NVFP4_ERR_SHAPE;
+    if ((m > 0 && k > 0 && !lora_a) || (n > 0 && !lora_b) || (m > 0 && !lora_u))
+        return NVFP4_ERR_NULL;
+    if ((lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)) || (lora_u && !aligned16(lora_u)))
+        return NVFP4_ERR_ALIGN;
+    if (!dtype_ok(y_dtype) || !rule_ok(rule) || (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
+        return NVFP4_ERR_DTYPE;
+    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n ||
+        (w_scale_layout == NVFP4_SCALE_2D && n % 16 != 0))
+        return NVFP4_ERR_SHAPE;
+    if (!w_alpha || (m > 0 && n > 0 && !y) || (m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!w_codes || !w_scales)))
+        return NVFP4_ERR_NULL;
+    if (ldx % 8 != 0 || (x && !aligned16(x)) || (y && !aligned_elem(y, y_dtype)) ||
+        (y_amax && ((uintptr_t)y_amax & 3u) != 0) || (w_codes && !aligned16(w_codes)) ||
+        (w_scales && !aligned16(w_scales)))
+        return NVFP4_ERR_ALIGN;
+    if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
+        return NVFP4_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlignWs) != 0)
+        return NVFP4_ERR_ALIGN;
+    uint8_t *ws = (uint8_t *)workspace;
+    float *alpha = (float *)ws;
+    float *partials = (float *)(ws + kAlignWs);
+    uint8_t *codes = ws + kAlignWs + round_up(kAmaxBytes, kAlignWs);
+    uint8_t *scales = codes + round_up((size_t)(m * k / 2), kAlignWs);
+    nvfp4_status_t st = do_quantize(x, NVFP4_BF16, m, k, ldx, NVFP4_ROW16, rule, nullptr, codes, scales, alpha,
+                                    partials, stream);
+    if (st != NVFP4_OK)
+        return st;
+    // U = x A^T (an empty contraction gives zeros)
+    st = launch_status(launch_lora_down((const uint16_t *)x, ldx, m, k, (const uint16_t *)lora_a, rank,
+                                        (uint16_t *)lora_u, stream));
+    if (st != NVFP4_OK)
+        return st;
+    GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};
+    GemmOperand B{w_codes, w_scales, w_alpha, w_scale_layout};
+    LoraBranch lb{(const uint16_t *)lora_u, (const uint16_t *)lora_b, rank, lora_scale};
+    return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, y_amax, stream, &lb));
+}
+
 // workspace: [alpha_dy][alpha_x] (256 B), [partials dy][partials x],
 //            [dy^T codes][dy^T scales][x^T codes][x^T scales]
 size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in)

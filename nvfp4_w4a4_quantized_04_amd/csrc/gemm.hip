@@ -45,7 +45,17 @@ struct GemmArgs {
     int c_bf16;
     int vec_ok;     // C pointer and ldc allow 4-element vector stores
     float *c_amax;  // optional: max |C| of the stored values (atomic max, zeroed before the launch)
+    // optional BF16 LoRA branch: C += lora_scale * U B^T, U [M][r], B [N][r]
+    const uint16_t *lora_u;
+    const uint16_t *lora_b;
+    int lora_r;
+    float lora_scale;
 };
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+// LDS row of a LoRA operand tile: r bf16 values + 16 bytes of padding.
+__host__ __device__ constexpr int lora_row_bytes(int r) { return 2 * r + 16; }
 
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f)
@@ -158,7 +168,7 @@ __device__ __forceinline__ void read_frags(const uint8_t *stage, const int (&a_f
         bf[j] = *reinterpret_cast<const half8v *>(stage + b_frag[j] + s * 32);
 }
 
-template <int TM, int TN, bool KFULL>
+template <int TM, int TN, bool KFULL, bool LORA>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_nvfp4(GemmArgs g)
 {
@@ -229,6 +239,25 @@ void k_gemm_nvfp4(GemmArgs g)
             else if (kt + S < nk)
                 __syncthreads();              // matches the consumers' last step
         });
+        if (LORA) {
+            // every fragment read of the main loop completed before the last
+            // barrier: stage the U rows of this tile and the B rows into LDS
+            const int pr = lora_row_bytes(g.lora_r);
+            const int vpr = g.lora_r / 8;                   // 16-byte vectors per row
+            for (int q = ptid; q < (BM + BN) * vpr; q += 256) {
+                const int row = q / vpr, cv = q - row * vpr;
+                const uint16_t *src;
+                if (row < BM) {
+                    const int gr = m0 + row < g.M ? m0 + row : g.M - 1;
+                    src = g.lora_u + (int64_t)gr * g.lora_r;
+                } else {
+                    const int gr = n0 + row - BM < g.N ? n0 + row - BM : g.N - 1;
+                    src = g.lora_b + (int64_t)gr * g.lora_r;
+                }
+                *reinterpret_cast<uint4 *>(lds + row * pr + cv * 16) = *reinterpret_cast<const uint4 *>(src + cv * 8);
+            }
+            __syncthreads();
+        }
         return;
     }
 
@@ -294,9 +323,38 @@ void k_gemm_nvfp4(GemmArgs g)
         }
     }
 
+    float scale = *g.a_alpha * *g.b_alpha;
+    if (LORA) {
+        // C = scale_q * acc + lora_scale * U B^T, accumulated as
+        // lora_scale * (acc * (scale_q / lora_scale) + U B^T) with bf16 MFMA
+        const float f = scale / g.lora_scale;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                acc[i][j] = acc[i][j] * f;
+        scale = g.lora_scale;
+        __syncthreads();                                  // the producers staged U and B
+        const int pr = lora_row_bytes(g.lora_r);
+        const uint8_t *ua_base = lds + (wm * 32 * TM + l32) * pr + half * 16;
+        const uint8_t *ub_base = lds + (BM + wn * 32 * TN + l32) * pr + half * 16;
+        for (int kk = 0; kk < g.lora_r; kk += 16) {
+            bf16x8v ua[TM];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                ua[i] = *reinterpret_cast<const bf16x8v *>(ua_base + i * 32 * pr + kk * 2);
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const bf16x8v ub = *reinterpret_cast<const bf16x8v *>(ub_base + j * 32 * pr + kk * 2);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, ua[i], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
     // epilogue: register r of lane l holds C[row = l%32][col = 8*(r/4) +
     // 4*(l/32) + r%4] of each 32x32 tile
-    const float scale = *g.a_alpha * *g.b_alpha;
     float amax = 0.0f;                  // max |C| over this lane's stored outputs
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -360,10 +418,18 @@ static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
     g.tiles_m = (g.M + 64 * TM - 1) / (64 * TM);
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
     const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
-    if (g.K % kBK == 0)
-        k_gemm_nvfp4<TM, TN, true><<<(unsigned)grid, 512, 0, s>>>(g);
-    else
-        k_gemm_nvfp4<TM, TN, false><<<(unsigned)grid, 512, 0, s>>>(g);
+    const bool kfull = g.K % kBK == 0;
+    if (g.lora_u) {
+        if (kfull)
+            k_gemm_nvfp4<TM, TN, true, true><<<(unsigned)grid, 512, 0, s>>>(g);
+        else
+            k_gemm_nvfp4<TM, TN, false, true><<<(unsigned)grid, 512, 0, s>>>(g);
+    } else {
+        if (kfull)
+            k_gemm_nvfp4<TM, TN, true, false><<<(unsigned)grid, 512, 0, s>>>(g);
+        else
+            k_gemm_nvfp4<TM, TN, false, false><<<(unsigned)grid, 512, 0, s>>>(g);
+    }
     return hipGetLastError();
 }
 
@@ -381,8 +447,72 @@ static double tile_cost(int64_t m, int64_t n, int tm, int tn)
 
 __global__ void k_zero_float(float *p) { *p = 0.0f; }
 
+// ------------------------------------------------ LoRA down projection
+
+// U [M][r] = RN_bf16(x [M][K] A^T), A [r][K], bf16, fp32 accumulation.  A
+// workgroup owns a 32 x 32 tile of U; its kLoraWaves waves split K and their
+// partial tiles are added in wave order through LDS (a fixed order).
+constexpr int kLoraWaves = 16;
+constexpr int kLoraBatch = 8;            // 16-k substeps whose fragments are loaded together
+
+__global__ __launch_bounds__(kLoraWaves * 64) void k_lora_down(const uint16_t *__restrict__ x, int64_t ldx, int M,
+                                                               int K, const uint16_t *__restrict__ a, int r,
+                                                               uint16_t *__restrict__ u)
+{
+    __shared__ float red[kLoraWaves][32 * 32];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int m0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+    const int mrow = m0 + l32 < M ? m0 + l32 : M - 1;     // rows past the end re-read the last row; never stored
+    const uint16_t *xp = x + (int64_t)mrow * ldx + half * 8;
+    const uint16_t *ap = a + (int64_t)(j0 + l32) * K + half * 8;
+    const int nsub = K / 16;
+    const int per = (nsub + kLoraWaves - 1) / kLoraWaves;
+    const int s0 = wave * per, s1 = s0 + per < nsub ? s0 + per : nsub;
+    float16v acc = float16v{};
+    for (int sb = s0; sb < s1; sb += kLoraBatch) {
+        bf16x8v fa[kLoraBatch], fx[kLoraBatch];
+#pragma unroll
+        for (int t = 0; t < kLoraBatch; t++) {
+            if (sb + t < s1) {
+                fa[t] = *reinterpret_cast<const bf16x8v *>(ap + (sb + t) * 16);
+                fx[t] = *reinterpret_cast<const bf16x8v *>(xp + (sb + t) * 16);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kLoraBatch; t++)
+            if (sb + t < s1)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t], fx[t], acc, 0, 0, 0);
+    }
+    // lane l, register q: U row m0 + l%32, column j0 + 8*(q/4) + 4*(l/32) + q%4
+#pragma unroll
+    for (int q = 0; q < 16; q++)
+        red[wave][l32 * 32 + 8 * (q >> 2) + 4 * half + (q & 3)] = acc[q];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 32 * 32; o += kLoraWaves * 64) {
+        float v = red[0][o];
+        for (int w = 1; w < kLoraWaves; w++)
+            v = v + red[w][o];
+        const int mm = m0 + o / 32, jj = j0 + (o & 31);
+        if (mm < M) {
+            const __bf16 h = (__bf16)v;
+            u[(int64_t)mm * r + jj] = __builtin_bit_cast(uint16_t, h);
+        }
+    }
+}
+
+hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
+                            uint16_t *u, hipStream_t s)
+{
+    if (m == 0)
+        return hipSuccess;
+    dim3 grid((unsigned)((m + 31) / 32), (unsigned)(r / 32));
+    k_lora_down<<<grid, kLoraWaves * 64, 0, s>>>(x, ldx, (int)m, (int)k, a, r, u);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
-                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s)
+                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s, const LoraBranch *lora)
 {
     if (c_amax) {
         // non-negative floats order like their bit patterns: the epilogue
@@ -396,6 +526,10 @@ hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, in
         return hipSuccess;
     GemmArgs g;
     g.c_amax = c_amax;
+    g.lora_u = lora ? lora->u : nullptr;
+    g.lora_b = lora ? lora->b : nullptr;
+    g.lora_r = lora ? lora->r : 0;
+    g.lora_scale = lora ? lora->scale : 1.0f;
     g.a_codes = a.codes; g.a_scales = a.scales; g.a_alpha = a.alpha; g.a2d = a.scale2d;
     g.b_codes = b.codes; g.b_scales = b.scales; g.b_alpha = b.alpha; g.b2d = b.scale2d;
     g.c = c; g.ldc = ldc; g.c_bf16 = cdtype == 1;

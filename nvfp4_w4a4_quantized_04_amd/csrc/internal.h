@@ -74,8 +74,21 @@ struct GemmOperand {
 hipError_t launch_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
                                    int64_t cols, uint8_t *codes_t, uint8_t *scales_t, float *alpha_t, hipStream_t s);
 
+// Optional BF16 LoRA branch added in the GEMM: C += scale * U B^T with U [m][r]
+// and B [n][r] bf16 (r a multiple of 16, at most 128).
+struct LoraBranch {
+    const uint16_t *u;
+    const uint16_t *b;
+    int r;
+    float scale;
+};
+
 // c_amax (optional): receives max |C| of the stored values
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
-                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s);
+                       int cdtype, int64_t ldc, float *c_amax, hipStream_t s, const LoraBranch *lora = nullptr);
+
+// U [m][r] = bf16(x A^T): x [m][k] bf16 (ld ldx), A [r][k] bf16; r % 32 == 0.
+hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
+                            uint16_t *u, hipStream_t s);
 
 }  // namespace nvfp4

@@ -136,6 +136,18 @@ def test_kv_consumer_validation_without_gpu():
     assert w(neg, 1, 128, FAKE, 1, 128, None) == 2
 
 
+def test_linear_lora_validation_without_gpu():
+    import nvfp4_w4a4_quantized_04_amd as m
+    f = m.lib.nvfp4_linear_lora
+    ok = (FAKE, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, FAKE)
+    assert f(*ok, 48, 1.0, FAKE, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 2      # rank not a multiple of 32
+    assert f(*ok, 256, 1.0, FAKE, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 2     # rank above 128
+    assert f(*ok, 64, 0.0, FAKE, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 2      # zero scale
+    assert f(*ok, 64, 1.0, None, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 1      # U buffer
+    assert f(*ok, 64, 1.0, FAKE + 8, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 3  # U alignment
+    assert f(*ok, 64, 1.0, FAKE, FAKE, 1, 48, None, FAKE, 10, None) == 5           # workspace
+
+
 def test_no_cpu_fallback():
     import torch
     import nvfp4_w4a4_quantized_04_amd as m

@@ -137,6 +137,37 @@ def test_training_dgrad_full():
     _check_gemm(dx32, dx16, A, Wt, 56)
 
 
+def test_qkv_projection_with_lora_full():
+    """The QKV projection with the rank-128 BF16 LoRA branch (alpha 128)."""
+    c = workloads.config2()
+    m, k = c["x"].shape
+    n = c["w"].shape[0]
+    rng = np.random.default_rng(58)
+    la = workloads.f32_to_bf16_bits((rng.standard_normal((128, k)) / np.sqrt(k)).astype(np.float32))
+    lb = workloads.f32_to_bf16_bits((rng.standard_normal((n, 128)) * 0.02).astype(np.float32))
+    print(f"[case] linear_lora m={m} k={k} n={n} r=128", flush=True)
+    W = oracle.quantize(c["w"], oracle.TILE16, oracle.FOUR_OVER_SIX)
+    A = oracle.quantize(c["x"], oracle.ROW16, oracle.FOUR_OVER_SIX)
+    Wd = packed_to_device(W)
+    y32, u = nv.linear_lora(dev_from_host(c["x"]), Wd, dev_from_host(la), dev_from_host(lb), 1.0, torch.float32)
+    y16, _ = nv.linear_lora(dev_from_host(c["x"]), Wd, dev_from_host(la), dev_from_host(lb), 1.0, torch.bfloat16)
+    torch.cuda.synchronize()
+    ug = host_bits(u)
+    ms, ns = _samples(m, n, 58)
+    base = oracle.gemm_f64_sampled(A, W, ms, ns)
+    uf = workloads.bf16_to_f32(ug).astype(np.float64)
+    bf = workloads.bf16_to_f32(lb).astype(np.float64)
+    ref = base + np.einsum("ij,ij->i", uf[ms], bf[ns])
+    err = rel_frobenius(host_bits(y32)[ms, ns], ref)
+    print(f"[parity] sampled rel Frobenius {err:.3e}", flush=True)
+    assert err <= GEMM_RTOL
+    assert np.array_equal(host_bits(y16), oracle.bf16_rne(host_bits(y32)))
+    # U: the first 64 and the last 64 rows against the exact sums
+    from tests.test_gpu_gemm import check_lora_u
+    check_lora_u(ug[:64], c["x"][:64], la)
+    check_lora_u(ug[-64:], c["x"][-64:], la)
+
+
 def test_kv_cache_full():
     c = workloads.config4()
     for name in ("k", "v"):

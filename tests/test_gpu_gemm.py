@@ -176,3 +176,44 @@ def test_dgrad(m, n, k):
     # the same product on the dequantized values in the original orientation
     ref2 = oracle.dequantize(A).astype(np.float64) @ oracle.dequantize(W).astype(np.float64)
     assert rel_frobenius(host_bits(dx), ref2) <= GEMM_RTOL
+
+
+def check_lora_u(ug: np.ndarray, x: np.ndarray, la: np.ndarray):
+    """U from the kernel is a correct bf16 rounding of a sum within the fp32
+    accumulation bound of x A^T: |U - exact| <= half a bf16 step of U plus
+    K * 2^-24 * sum |x a|; and it equals the oracle's rounding of the exact
+    sum except where the two sums straddle a rounding point (rare)."""
+    xf = workloads.bf16_to_f32(x).astype(np.float64)
+    af = workloads.bf16_to_f32(la).astype(np.float64)
+    exact = xf @ af.T
+    bound = xf.shape[1] * 2.0 ** -24 * (np.abs(xf) @ np.abs(af).T)
+    u = workloads.bf16_to_f32(ug).astype(np.float64)
+    step = np.abs(u) * 2.0 ** -7                       # one bf16 step at |u| (or more)
+    assert np.all(np.abs(u - exact) <= 0.5 * step + bound + 1e-300)
+    uref = oracle.lora_down_bf16(x, la)
+    assert np.mean(ug == uref) >= 0.99
+
+
+@pytest.mark.parametrize("m,n,k,r", [(300, 384, 512, 128), (17, 64, 48, 32), (1000, 1040, 272, 64)])
+def test_linear_lora(m, n, k, r):
+    """W4A4 linear + BF16 LoRA branch: U = bf16(x A^T) checked against the
+    exact sums (check_lora_u), and y against the fp64 reference built on the
+    kernel's U."""
+    print(f"[case] linear_lora m={m} n={n} k={k} r={r}", flush=True)
+    rng = np.random.default_rng(m + n + k + r)
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    la = workloads.f32_to_bf16_bits((rng.standard_normal((r, k)) / np.sqrt(k)).astype(np.float32))
+    lb = workloads.f32_to_bf16_bits((rng.standard_normal((n, r)) * 0.02).astype(np.float32))
+    W = oracle.quantize(w, oracle.TILE16, 1)
+    Wd = packed_to_device(W)
+    scale = 0.75
+    y, u = nv.linear_lora(dev_from_host(x), Wd, dev_from_host(la), dev_from_host(lb), scale, torch.float32)
+    y16, _ = nv.linear_lora(dev_from_host(x), Wd, dev_from_host(la), dev_from_host(lb), scale, torch.bfloat16)
+    torch.cuda.synchronize()
+    ug = host_bits(u)
+    check_lora_u(ug, x, la)
+    A = oracle.quantize(x, oracle.ROW16, 1)
+    ref = oracle.linear_lora_f64(A, W, ug, lb, scale)
+    assert rel_frobenius(host_bits(y), ref) <= GEMM_RTOL
+    assert np.array_equal(host_bits(y16), oracle.bf16_rne(host_bits(y)))
