@@ -273,10 +273,11 @@ def bench_extra(nv, workloads, iters):
     la = (torch.randn((r, k), generator=g, device="cuda") / k ** 0.5).to(torch.bfloat16)
     lb = (torch.randn((n, r), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     u = torch.empty((m, r), dtype=torch.bfloat16, device="cuda")
+    lws = torch.empty(nv.lib.nvfp4_linear_lora_workspace_size(m, k, r), dtype=torch.uint8, device="cuda")
 
     def lora_step(i):
         x_, w_, y_, ws_ = sets[i % len(sets)]
-        nv.linear_lora(x_, w_, la, lb, 1.0, torch.bfloat16, out=y_, workspace=ws_, u=u)
+        nv.linear_lora(x_, w_, la, lb, 1.0, torch.bfloat16, out=y_, workspace=lws, u=u)
 
     ms = time_events(lora_step, iters)
     out["qkv_lora_r128_m2640_k3072_n9216"] = {

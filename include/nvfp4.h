@@ -201,12 +201,16 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
  * that receives U (x A^T with fp32 accumulation, rounded once to bf16, as a
  * bf16 linear layer computes it).  The rank-r update runs on bf16 MFMA in the
  * same GEMM launch after the NVFP4 contraction; fp32 accumulation.  Other
- * arguments and the workspace as nvfp4_linear.
+ * arguments as nvfp4_linear; workspace >= nvfp4_linear_lora_workspace_size().
  * Source: "LoRA parameterization" (W ~ Dequant(Q(W0)) + (alpha/r) B A, rank
  * 128, alpha 128, BF16 adapters) and the NVFP4 Inference section (the
  * adapters kept as a separate BF16 branch on the quantized backbone) of the
  * architecture walkthrough page.
  */
+/* Workspace of nvfp4_linear_lora: nvfp4_linear's plus the partial sums of
+ * the down projection (at most 8 * m * rank floats). */
+size_t nvfp4_linear_lora_workspace_size(int64_t m, int64_t k, int rank);
+
 nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,
                                  const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                  int w_scale_layout, int64_t n, const void *lora_a, const void *lora_b, int rank,

@@ -80,6 +80,8 @@ def _load():
     L.nvfp4_kv_quantize_smoothed.argtypes = [P, i32, i64, i64, i32, P, P, P, P, P, sz, P]
     L.nvfp4_kv_dequantize_window.restype = i32
     L.nvfp4_kv_dequantize_window.argtypes = [ctypes.POINTER(KvSegment), i32, i64, P, i32, i64, P]
+    L.nvfp4_linear_lora_workspace_size.restype = sz
+    L.nvfp4_linear_lora_workspace_size.argtypes = [i64, i64, i32]
     L.nvfp4_linear_lora.restype = i32
     L.nvfp4_linear_lora.argtypes = [P, i64, i64, i64, i32, P, P, P, i32, i64, P, P, i32, ctypes.c_float, P, P, i32,
                                     i64, P, P, sz, P]
@@ -96,7 +98,8 @@ EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspac
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
             "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",
-            "nvfp4_kv_dequantize_window", "nvfp4_linear_lora"]
+            "nvfp4_kv_dequantize_window", "nvfp4_linear_lora",
+            "nvfp4_linear_lora_workspace_size"]
 
 
 def _check(fn: str, st: int):
@@ -433,7 +436,7 @@ def linear_lora(x: torch.Tensor, w: NVFP4Tensor, lora_a: torch.Tensor, lora_b: t
     if u is None:
         u = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
-        workspace = linear_workspace(m, k, x.device)
+        workspace = torch.empty(lib.nvfp4_linear_lora_workspace_size(m, k, r), dtype=torch.uint8, device=x.device)
     _check("nvfp4_linear_lora", lib.nvfp4_linear_lora(
         _ptr(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n, _ptr(lora_a), _ptr(lora_b), r,
         float(lora_scale), _ptr(u), _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out),

@@ -227,6 +227,13 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
     return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, y_amax, stream));
 }
 
+size_t nvfp4_linear_lora_workspace_size(int64_t m, int64_t k, int rank)
+{
+    if (m < 0 || k < 0 || rank < 0)
+        return 0;
+    return nvfp4_linear_workspace_size(m, k) + round_up((size_t)kLoraMaxSlicesAbi * m * rank * 4, kAlignWs);
+}
+
 nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,
                                  const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
                                  int w_scale_layout, int64_t n, const void *lora_a, const void *lora_b, int rank,
@@ -252,7 +259,8 @@ nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ld
         (y_amax && ((uintptr_t)y_amax & 3u) != 0) || (w_codes && !aligned16(w_codes)) ||
         (w_scales && !aligned16(w_scales)))
         return NVFP4_ERR_ALIGN;
-    if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
+    static_assert(kLoraMaxSlicesAbi >= 1, "slices");
+    if (!workspace || workspace_bytes < nvfp4_linear_lora_workspace_size(m, k, rank))
         return NVFP4_ERR_WORKSPACE;
     if (((uintptr_t)workspace % kAlignWs) != 0)
         return NVFP4_ERR_ALIGN;
@@ -261,13 +269,14 @@ nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ld
     float *partials = (float *)(ws + kAlignWs);
     uint8_t *codes = ws + kAlignWs + round_up(kAmaxBytes, kAlignWs);
     uint8_t *scales = codes + round_up((size_t)(m * k / 2), kAlignWs);
+    float *lora_part = (float *)(ws + nvfp4_linear_workspace_size(m, k));
     nvfp4_status_t st = do_quantize(x, NVFP4_BF16, m, k, ldx, NVFP4_ROW16, rule, nullptr, codes, scales, alpha,
                                     partials, stream);
     if (st != NVFP4_OK)
         return st;
     // U = x A^T (an empty contraction gives zeros)
     st = launch_status(launch_lora_down((const uint16_t *)x, ldx, m, k, (const uint16_t *)lora_a, rank,
-                                        (uint16_t *)lora_u, stream));
+                                        (uint16_t *)lora_u, lora_part, stream));
     if (st != NVFP4_OK)
         return st;
     GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};

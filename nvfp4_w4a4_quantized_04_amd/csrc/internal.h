@@ -87,8 +87,11 @@ struct LoraBranch {
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
                        int cdtype, int64_t ldc, float *c_amax, hipStream_t s, const LoraBranch *lora = nullptr);
 
-// U [m][r] = bf16(x A^T): x [m][k] bf16 (ld ldx), A [r][k] bf16; r % 32 == 0.
+// U [m][r] = bf16(x A^T): x [m][k] bf16 (ld ldx), A [r][k] bf16; r % 32 == 0,
+// r <= 128.  partials: lora_slices(m, k) * m * r floats of scratch.
+int lora_slices(int64_t m, int64_t k);
+constexpr int kLoraMaxSlicesAbi = 8;
 hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
-                            uint16_t *u, hipStream_t s);
+                            uint16_t *u, float *partials, hipStream_t s);
 
 }  // namespace nvfp4

@@ -146,6 +146,7 @@ def test_linear_lora_validation_without_gpu():
     assert f(*ok, 64, 1.0, None, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 1      # U buffer
     assert f(*ok, 64, 1.0, FAKE + 8, FAKE, 1, 48, None, FAKE, 1 << 30, None) == 3  # U alignment
     assert f(*ok, 64, 1.0, FAKE, FAKE, 1, 48, None, FAKE, 10, None) == 5           # workspace
+    assert m.lib.nvfp4_linear_lora_workspace_size(32, 64, 64) >= m.lib.nvfp4_linear_workspace_size(32, 64) + 8 * 32 * 64 * 4
 
 
 def test_no_cpu_fallback():
