@@ -244,17 +244,34 @@ void k_gemm_nvfp4(GemmArgs g)
             // barrier: stage the U rows of this tile and the B rows into LDS
             const int pr = lora_row_bytes(g.lora_r);
             const int vpr = g.lora_r / 8;                   // 16-byte vectors per row
-            for (int q = ptid; q < (BM + BN) * vpr; q += 256) {
-                const int row = q / vpr, cv = q - row * vpr;
-                const uint16_t *src;
-                if (row < BM) {
-                    const int gr = m0 + row < g.M ? m0 + row : g.M - 1;
-                    src = g.lora_u + (int64_t)gr * g.lora_r;
-                } else {
-                    const int gr = n0 + row - BM < g.N ? n0 + row - BM : g.N - 1;
-                    src = g.lora_b + (int64_t)gr * g.lora_r;
+            const int total = (BM + BN) * vpr;
+            constexpr int kBatch = 8;                       // loads in flight per thread
+            for (int q0 = ptid; q0 < total; q0 += 256 * kBatch) {
+                uint4 v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; u++) {
+                    const int q = q0 + u * 256;
+                    if (q < total) {
+                        const int row = q / vpr, cv = q - row * vpr;
+                        const uint16_t *src;
+                        if (row < BM) {
+                            const int gr = m0 + row < g.M ? m0 + row : g.M - 1;
+                            src = g.lora_u + (int64_t)gr * g.lora_r;
+                        } else {
+                            const int gr = n0 + row - BM < g.N ? n0 + row - BM : g.N - 1;
+                            src = g.lora_b + (int64_t)gr * g.lora_r;
+                        }
+                        v[u] = *reinterpret_cast<const uint4 *>(src + cv * 8);
+                    }
                 }
-                *reinterpret_cast<uint4 *>(lds + row * pr + cv * 16) = *reinterpret_cast<const uint4 *>(src + cv * 8);
+#pragma unroll
+                for (int u = 0; u < kBatch; u++) {
+                    const int q = q0 + u * 256;
+                    if (q < total) {
+                        const int row = q / vpr, cv = q - row * vpr;
+                        *reinterpret_cast<uint4 *>(lds + row * pr + cv * 16) = v[u];
+                    }
+                }
             }
             __syncthreads();
         }
