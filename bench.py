@@ -42,8 +42,8 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
 # counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
 # counters read for a plain 256 MiB device copy.  They hold for the GEMM
 # source they were taken with only: null once gemm.hip has changed.
-GEMM_TRAFFIC = {"gemm_src_sha256": "4e45716f04ddb85772882a24dc970e5bc937a3d3701391b9f65a55efbf705fde",
-                "bytes_per_launch": 140371628}
+GEMM_TRAFFIC = {"gemm_src_sha256": "b986e261a4c8e59caae8e03089b6ecd6bf45c84ff400e8eec96d5da2b25eed1b",
+                "bytes_per_launch": 140387584}
 
 
 def gemm_traffic():
