@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 import oracle
+import workloads
 
 GEMM_RTOL = 1e-5          # relative Frobenius bound on fp32 GEMM outputs
 
@@ -51,3 +52,19 @@ def packed_to_device(p: oracle.Packed):
     import nvfp4_w4a4_quantized_04_amd as nv
     return nv.NVFP4Tensor(torch.from_numpy(p.codes.copy()).cuda(), torch.from_numpy(p.scales.copy()).cuda(),
                           torch.tensor([p.alpha], dtype=torch.float32).cuda(), p.rows, p.cols, p.block)
+
+
+def check_lora_u(ug: np.ndarray, x: np.ndarray, la: np.ndarray):
+    """U from the kernel is a correct bf16 rounding of a sum within the fp32
+    accumulation bound of x A^T: |U - exact| <= half a bf16 step of U plus
+    K * 2^-24 * sum |x a|; and it equals the oracle's rounding of the exact
+    sum except where the two sums straddle a rounding point (rare)."""
+    xf = workloads.bf16_to_f32(x).astype(np.float64)
+    af = workloads.bf16_to_f32(la).astype(np.float64)
+    exact = xf @ af.T
+    bound = xf.shape[1] * 2.0 ** -24 * (np.abs(xf) @ np.abs(af).T)
+    u = workloads.bf16_to_f32(ug).astype(np.float64)
+    step = np.abs(u) * 2.0 ** -7                       # one bf16 step at |u| (or more)
+    assert np.all(np.abs(u - exact) <= 0.5 * step + bound + 1e-300)
+    uref = oracle.lora_down_bf16(x, la)
+    assert np.mean(ug == uref) >= 0.99

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import GEMM_RTOL, assert_packed_equal, dev_from_host, host_bits, packed_to_device, rel_frobenius
+from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, check_lora_u, dev_from_host, host_bits,
+                               packed_to_device, rel_frobenius)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -163,7 +164,6 @@ def test_qkv_projection_with_lora_full():
     assert err <= GEMM_RTOL
     assert np.array_equal(host_bits(y16), oracle.bf16_rne(host_bits(y32)))
     # U: the first 64 and the last 64 rows against the exact sums
-    from tests.test_gpu_gemm import check_lora_u
     check_lora_u(ug[:64], c["x"][:64], la)
     check_lora_u(ug[-64:], c["x"][-64:], la)
 

@@ -8,8 +8,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, dev_from_host, host_bits, packed_to_device,
-                               rel_frobenius)
+from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, check_lora_u, dev_from_host, host_bits,
+                               packed_to_device, rel_frobenius)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,22 +176,6 @@ def test_dgrad(m, n, k):
     # the same product on the dequantized values in the original orientation
     ref2 = oracle.dequantize(A).astype(np.float64) @ oracle.dequantize(W).astype(np.float64)
     assert rel_frobenius(host_bits(dx), ref2) <= GEMM_RTOL
-
-
-def check_lora_u(ug: np.ndarray, x: np.ndarray, la: np.ndarray):
-    """U from the kernel is a correct bf16 rounding of a sum within the fp32
-    accumulation bound of x A^T: |U - exact| <= half a bf16 step of U plus
-    K * 2^-24 * sum |x a|; and it equals the oracle's rounding of the exact
-    sum except where the two sums straddle a rounding point (rare)."""
-    xf = workloads.bf16_to_f32(x).astype(np.float64)
-    af = workloads.bf16_to_f32(la).astype(np.float64)
-    exact = xf @ af.T
-    bound = xf.shape[1] * 2.0 ** -24 * (np.abs(xf) @ np.abs(af).T)
-    u = workloads.bf16_to_f32(ug).astype(np.float64)
-    step = np.abs(u) * 2.0 ** -7                       # one bf16 step at |u| (or more)
-    assert np.all(np.abs(u - exact) <= 0.5 * step + bound + 1e-300)
-    uref = oracle.lora_down_bf16(x, la)
-    assert np.mean(ug == uref) >= 0.99
 
 
 @pytest.mark.parametrize("m,n,k,r", [(300, 384, 512, 128), (17, 64, 48, 32), (1000, 1040, 272, 64)])
