@@ -564,7 +564,7 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const float *__restrict__ p
 int lora_slices(int64_t m, int64_t k)
 {
     const int64_t mt = (m + 31) / 32;
-    int64_t sl = (256 + mt - 1) / mt;               // about one workgroup per CU
+    int64_t sl = (768 + mt - 1) / mt;               // about three workgroups per CU
     const int64_t steps = (k + 63) / 64;
     if (sl > steps) sl = steps;
     if (sl > kLoraMaxSlicesAbi) sl = kLoraMaxSlicesAbi;
