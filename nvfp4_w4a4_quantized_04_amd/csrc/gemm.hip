@@ -15,8 +15,10 @@
 //   producers (waves 4-7) fetch packed stages (0.5 B codes + 1/16 B scale per
 //     element) from HBM PD steps ahead into registers, decode them with
 //     v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16 by the E4M3 block scale (both
-//     exact) and write fp16 tiles into LDS (double buffered, rows padded to
-//     144 B so 16 consecutive rows hit distinct banks);
+//     exact; the convert's own scale operand contributes only its exponent,
+//     so it cannot apply an E4M3 scale) and write fp16 tiles into LDS (double
+//     buffered, rows padded to 144 B so 16 consecutive rows hit distinct
+//     banks);
 //   consumers (waves 0-3, 2x2 grid) hold the fp32 accumulators, read MFMA
 //     fragments from LDS one 16-k substep ahead and issue the MFMAs.
 // The decode VALU work of one wave then overlaps the MFMA work of the other
@@ -463,134 +465,6 @@ static double tile_cost(int64_t m, int64_t n, int tm, int tn)
 }
 
 __global__ void k_zero_float(float *p) { *p = 0.0f; }
-
-// ------------------------------------------------ LoRA down projection
-
-// U [M][r] = RN_bf16(x [M][K] A^T), A [r][K], bf16 operands, fp32 sums.
-// Stage 1: workgroup (m tile of 32 rows, K slice) stages 64-k steps of x and A
-// in LDS with 16-byte coalesced loads (the next step's loads in flight) and
-// accumulates a 32 x r partial with 32x32x16 bf16 MFMA, one 32-column block
-// per wave.  Stage 2 adds the K-slice partials in slice order and rounds once.
-constexpr int kLoraRowB = 64 * 2 + 16;   // LDS bytes per staged row (64 k + pad)
-
-
-__global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict__ x, int64_t ldx, int M, int K,
-                                                      const uint16_t *__restrict__ a, int r, int kslice,
-                                                      float *__restrict__ part)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(32 + 128) * kLoraRowB];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int l32 = lane & 31, half = lane >> 5;
-    const int m0 = blockIdx.x * 32;
-    const int kb = blockIdx.y * kslice, ke = kb + kslice < K ? kb + kslice : K;
-    const int nrows = 32 + r;                      // staged rows: 32 of x, r of A
-    const int chunks = nrows * 8;                  // 16-byte chunks per 64-k step
-    float16v acc = float16v{};
-    const bool active = wave * 32 < r;
-    auto fetch = [&](int k0, uint4 (&v)[5]) {
-#pragma unroll
-        for (int u = 0; u < 5; u++) {
-            const int q = tid + u * 256;
-            v[u] = make_uint4(0, 0, 0, 0);
-            if (q < chunks) {
-                const int row = q >> 3, c = q & 7;
-                const int k = k0 + c * 8;
-                if (k < ke) {
-                    const uint16_t *src = row < 32 ? x + (int64_t)(m0 + row < M ? m0 + row : M - 1) * ldx
-                                                   : a + (int64_t)(row - 32) * K;
-                    v[u] = *reinterpret_cast<const uint4 *>(src + k);
-                }
-            }
-        }
-    };
-    auto stash = [&](uint8_t *buf, const uint4 (&v)[5]) {
-#pragma unroll
-        for (int u = 0; u < 5; u++) {
-            const int q = tid + u * 256;
-            if (q < chunks)
-                *reinterpret_cast<uint4 *>(buf + (q >> 3) * kLoraRowB + (q & 7) * 16) = v[u];
-        }
-    };
-    uint4 v[5];
-    int buf = 0;
-    if (kb < ke) {
-        fetch(kb, v);
-        stash(lds[0], v);
-    }
-    __syncthreads();
-    for (int k0 = kb; k0 < ke; k0 += 64) {
-        const bool more = k0 + 64 < ke;
-        if (more)
-            fetch(k0 + 64, v);                     // in flight under this step's MFMAs
-        if (active) {
-            const uint8_t *st = lds[buf];
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                const bf16x8v fa = *reinterpret_cast<const bf16x8v *>(st + (32 + wave * 32 + l32) * kLoraRowB + s * 32 + half * 16);
-                const bf16x8v fx = *reinterpret_cast<const bf16x8v *>(st + l32 * kLoraRowB + s * 32 + half * 16);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fx, acc, 0, 0, 0);
-            }
-        }
-        if (more)
-            stash(lds[buf ^ 1], v);
-        __syncthreads();
-        buf ^= 1;
-    }
-    // lane l, register q: row m0 + l%32, column 32*wave + 8*(q/4) + 4*(l/32) + q%4
-    if (active) {
-        float *dst = part + ((int64_t)blockIdx.y * M + m0 + l32) * r + wave * 32 + 4 * half;
-        if (m0 + l32 < M) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-                *reinterpret_cast<float4 *>(dst + 8 * q4) =
-                    make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void k_lora_reduce(const float *__restrict__ part, int slices, int64_t n,
-                                                     uint16_t *__restrict__ u)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n)
-        return;
-    float v = slices > 0 ? part[i] : 0.0f;
-    for (int s = 1; s < slices; s++)
-        v = v + part[s * n + i];
-    const __bf16 h = (__bf16)v;
-    u[i] = __builtin_bit_cast(uint16_t, h);
-}
-
-int lora_slices(int64_t m, int64_t k)
-{
-    const int64_t mt = (m + 31) / 32;
-    int64_t sl = (768 + mt - 1) / mt;               // about three workgroups per CU
-    const int64_t steps = (k + 63) / 64;
-    if (sl > steps) sl = steps;
-    if (sl > kLoraMaxSlicesAbi) sl = kLoraMaxSlicesAbi;
-    return (int)(sl < 1 ? 1 : sl);
-}
-
-hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
-                            uint16_t *u, float *partials, hipStream_t s)
-{
-    if (m == 0)
-        return hipSuccess;
-    const int sl = lora_slices(m, k);
-    const int64_t steps = (k + 63) / 64;
-    const int kslice = (int)((steps + sl - 1) / sl * 64);
-    if (k > 0) {
-        dim3 grid((unsigned)((m + 31) / 32), (unsigned)sl);
-        k_lora_partial<<<grid, 256, 0, s>>>(x, ldx, (int)m, (int)k, a, r, kslice, partials);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    const int64_t n = m * r;
-    // k == 0: no partial was written and U is zero
-    k_lora_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, k > 0 ? sl : 0, n, u);
-    return hipGetLastError();
-}
 
 hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, int64_t n, int64_t k, void *c,
                        int cdtype, int64_t ldc, float *c_amax, hipStream_t s, const LoraBranch *lora)
