@@ -15,18 +15,27 @@
 
 namespace nvfp4 {
 
-// Reduce the partial maxima (or read one amax) into alpha; all threads of the
-// block get the same value.  Must be called by every thread of the block.
-__device__ __forceinline__ float block_alpha(const float *__restrict__ amax_src, int n_amax)
+// alpha from the amax partial maxima (n_amax > 1) or from one amax
+// (n_amax == 1), in two phases.  Vector loads complete in order, so a partial
+// loaded after a kernel's data loads would wait for all of them: alpha_issue
+// starts the partial load first, the kernel then issues its data loads, and
+// alpha_finish reduces while the data is in flight.  Every thread of the
+// block (kQuantThreads) must call both; all get the same alpha.
+static_assert(kMaxAmaxPartials <= kQuantThreads, "one partial per thread");
+
+__device__ __forceinline__ float alpha_issue(const float *__restrict__ amax_src, int n_amax)
+{
+    return n_amax > 1 && (int)threadIdx.x < n_amax ? amax_src[threadIdx.x] : 0.0f;
+}
+
+__device__ __forceinline__ float alpha_finish(float part, const float *__restrict__ amax_src, int n_amax)
 {
     __shared__ float red[kQuantThreads / 64];
-    float a = 0.0f;
+    float a;
     if (n_amax == 1) {
         a = amax_src[0];
     } else {
-        for (int i = threadIdx.x; i < n_amax; i += kQuantThreads)
-            a = fmaxf(a, amax_src[i]);
-        a = wave_max(a);
+        a = wave_max(part);
         if ((threadIdx.x & 63) == 0)
             red[threadIdx.x >> 6] = a;
         __syncthreads();
@@ -68,7 +77,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, 
         const int64_t n = rows * cols;
         const int64_t nv = n / V;
         constexpr int64_t kIter = (int64_t)kAmaxThreads * kAmaxUnroll;   // vectors per workgroup iteration
-        const int64_t per_wg = ((nv + gridDim.x - 1) / gridDim.x + kIter - 1) / kIter * kIter;
+        const int64_t per_wg = ((nv + gridDim.x - 1) / gridDim.x + kAmaxThreads - 1) / kAmaxThreads * kAmaxThreads;
         const int64_t beg = (int64_t)blockIdx.x * per_wg;
         const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
@@ -123,8 +132,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
     const int64_t nb = rows * bpr;
     const bool flat = ldx == bpr * 16;
     const int64_t b0 = (int64_t)blockIdx.x * (kQuantThreads * kRowBlocks) + threadIdx.x;
-    // issue the data loads first; alpha and the kappa table are set up while
-    // they are in flight
+    // partial load, then the data loads; alpha and the kappa table are set up
+    // while the data is in flight
+    const float apart = alpha_issue(amax_src, n_amax);
     float v[kRowBlocks][16];
 #pragma unroll
     for (int j = 0; j < kRowBlocks; j++) {
@@ -140,7 +150,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
             load16(x + off, v[j]);
         }
     }
-    const float alpha = block_alpha(amax_src, n_amax);
+    const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
@@ -182,10 +192,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
     __shared__ __attribute__((aligned(16))) uint8_t cpark[kColCols * kColCodePitch];
     __shared__ __attribute__((aligned(16))) uint8_t spark[kColCols * kColGroupRB];
 
-    const float alpha = block_alpha(amax_src, n_amax);
-    build_kappa_table(ktab, alpha);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-        *alpha_out = alpha;
+    const float apart = alpha_issue(amax_src, n_amax);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t nrb = rows / 16;
@@ -216,11 +223,21 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
         }
     };
 
-    for (int64_t g0 = (int64_t)blockIdx.y * kColGroupRB; g0 < nrb; g0 += (int64_t)gridDim.y * kColGroupRB) {
+    // the first group's first row-block is in flight while alpha and the
+    // kappa table are set up
+    Pair v[2][16];
+    const int64_t gfirst = (int64_t)blockIdx.y * kColGroupRB;
+    if (gfirst < nrb && gfirst + wave < nrb)
+        load_block(gfirst + wave, v[0]);
+    const float alpha = alpha_finish(apart, amax_src, n_amax);
+    build_kappa_table(ktab, alpha);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *alpha_out = alpha;
+
+    for (int64_t g0 = gfirst; g0 < nrb; g0 += (int64_t)gridDim.y * kColGroupRB) {
         const int ng = nrb - g0 < kColGroupRB ? (int)(nrb - g0) : kColGroupRB;
-        Pair v[2][16];
         int64_t rb = g0 + wave;
-        if (wave < ng)
+        if (g0 != gfirst && wave < ng)
             load_block(rb, v[0]);
 #pragma unroll
         for (int st = 0; st < kSteps; st++) {
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restr
                                                                 float *__restrict__ alpha_out)
 {
     __shared__ float ktab[128];
-    const float alpha = block_alpha(amax_src, n_amax);
+    const float alpha = alpha_finish(alpha_issue(amax_src, n_amax), amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
@@ -544,13 +561,14 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_quant_smoothed(const T *__
     __shared__ float ktab[128];
     const int64_t nb = vectors << g_log2;
     const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    const float apart = alpha_issue(amax_src, n_amax);
     float f[16];
     float mean = 0.0f;
     if (b < nb) {
         load16(x + b * 16, f);
         mean = means[b >> g_log2];
     }
-    const float alpha = block_alpha(amax_src, n_amax);
+    const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
