@@ -12,8 +12,11 @@ The same JSON line also carries
                 against the fp16 MFMA peak (its operands are exact fp16);
   kv            NVFP4 KV-cache quantize and dequantize of K and V bf16
                 [24, 18480, 128] in GB/s of algorithmic bytes, and against HBM;
-  extra         the FFN pair and the long-sequence training shapes (forward,
-                weight gradient, data gradient);
+  extra         the FFN pair, the QKV projection with a rank-128 LoRA
+                branch, the long-sequence training shapes (forward, weight
+                gradient with and without the Hadamard transform, data
+                gradient), and for context the vendor library's dense
+                fp16/bf16 GEMM on the QKV shape;
   cpu_baseline  the CPU oracle (fp32 quantizer, fp64 GEMM) on the full QKV
                 step on the host cores.
 
@@ -42,8 +45,8 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
 # counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
 # counters read for a plain 256 MiB device copy.  They hold for the GEMM
 # source they were taken with only: null once gemm.hip has changed.
-GEMM_TRAFFIC = {"gemm_src_sha256": "b986e261a4c8e59caae8e03089b6ecd6bf45c84ff400e8eec96d5da2b25eed1b",
-                "bytes_per_launch": 140387584}
+GEMM_TRAFFIC = {"gemm_src_sha256": "387381b0e927d14756dece4697e8c4eb0469bb0c36a090293f68972cdf78692a",
+                "bytes_per_launch": 140391043}
 
 
 def gemm_traffic():
@@ -320,6 +323,25 @@ def bench_extra(nv, workloads, iters):
     ms = time_events(dg, iters)
     out["train_dgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
                                              "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    del x, dy, dw, ws, w, wt, dx, lws
+    torch.cuda.empty_cache()
+    # context: the vendor library's dense fp16 / bf16 GEMM (torch.matmul,
+    # hipBLASLt) on the QKV shape, with 16-bit operands and no quantization
+    m, k, n = 2640, 3072, 9216
+    for dt, tag in ((torch.float16, "fp16"), (torch.bfloat16, "bf16")):
+        pairs = [(torch.randn((m, k), generator=g, device="cuda").to(dt),
+                  torch.randn((n, k), generator=g, device="cuda").to(dt)) for _ in range(3)]
+        c = torch.empty((m, n), dtype=dt, device="cuda")
+
+        def mm(i):
+            a_, b_ = pairs[i % 3]
+            torch.matmul(a_, b_.t(), out=c)
+
+        ms = time_events(mm, iters)
+        out[f"context_vendor_{tag}_gemm_m2640_k3072_n9216"] = {
+            "ms": round(ms, 4), "TFLOPs": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1),
+            "note": "torch.matmul (hipBLASLt), dense 16-bit operands: context, not this library"}
+        del pairs, c
     return out
 
 

@@ -113,7 +113,7 @@ def test_hip_build_script_loads_without_the_library():
     import __graft_entry__ as ge
     mod = ge._hip_build_module()
     names = [os.path.basename(p) for p in mod.sources()]
-    assert {"api.hip", "gemm.hip", "quant.hip", "pack.hip"} <= set(names)
+    assert {"api.hip", "gemm.hip", "lora.hip", "quant.hip", "pack.hip"} <= set(names)
 
 
 def test_kv_consumer_validation_without_gpu():
