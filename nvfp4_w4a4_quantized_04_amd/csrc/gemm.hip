@@ -23,6 +23,11 @@
 //     fragments from LDS one 16-k substep ahead and issue the MFMAs.
 // The decode VALU work of one wave then overlaps the MFMA work of the other
 // wave on the same SIMD.  One barrier per 64-k step hands a stage over.
+// Epilogue (bf16 C): the consumers write the scaled, rounded tile into the
+// idle stage buffers and all eight waves store it as whole 16-byte row
+// chunks; storing the 32x32 fragments directly leaves every store
+// instruction 16 bytes in each of 32 rows, which is slower when every
+// workgroup of a round writes its tile at once.
 // Workgroup tile (64 TM) x (64 TN), BK = 64; consumer wave tile (32 TM) x (32 TN).
 #include "internal.h"
 
@@ -46,6 +51,7 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int c_bf16;
     int vec_ok;     // C pointer and ldc allow 4-element vector stores
+    int stage_ok;   // bf16 C, 16-byte aligned rows, N % 8 == 0: epilogue staged through LDS
     float *c_amax;  // optional: max |C| of the stored values (atomic max, zeroed before the launch)
     // optional BF16 LoRA branch: C += lora_scale * U B^T, U [M][r], B [N][r]
     const uint16_t *lora_u;
@@ -170,6 +176,29 @@ __device__ __forceinline__ void read_frags(const uint8_t *stage, const int (&a_f
         bf[j] = *reinterpret_cast<const half8v *>(stage + b_frag[j] + s * 32);
 }
 
+// Row pitch of the bf16 C tile staged in LDS for the epilogue (16 bytes of
+// padding per row).
+__host__ __device__ constexpr int c_pitch(int bn) { return bn * 2 + 16; }
+
+// All 512 threads copy the staged bf16 tile [BM][BN] to C, 16 bytes per
+// store, consecutive threads along a row.
+template <int BM, int BN>
+__device__ __forceinline__ void store_staged_c(const GemmArgs &g, const uint8_t *lds, int m0, int n0, int tid)
+{
+    constexpr int kChunks = BN / 8;                     // 16-byte chunks per row
+    static_assert((BM * kChunks) % 512 == 0, "whole chunks per thread");
+#pragma unroll
+    for (int u = 0; u < BM * kChunks / 512; u++) {
+        const int idx = tid + 512 * u;
+        const int r = idx / kChunks, c = idx - r * kChunks;
+        const int row = m0 + r, col = n0 + c * 8;
+        if (row < g.M && col < g.N) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(lds + r * c_pitch(BN) + c * 16);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(g.c) + (int64_t)row * g.ldc + col) = v;
+        }
+    }
+}
+
 template <int TM, int TN, bool KFULL, bool LORA>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_nvfp4(GemmArgs g)
@@ -177,6 +206,7 @@ void k_gemm_nvfp4(GemmArgs g)
     constexpr int BM = 64 * TM, BN = 64 * TN;
     constexpr int kStage = (BM + BN) * kLdsRow;
     constexpr int PD = kPrefetch;
+    static_assert(BM * c_pitch(BN) <= 2 * kStage, "the staged C tile fits in the stage buffers");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
     const int tid = threadIdx.x;
@@ -277,6 +307,10 @@ void k_gemm_nvfp4(GemmArgs g)
             }
             __syncthreads();
         }
+        if (!LORA && g.stage_ok) {
+            __syncthreads();                              // the consumers staged C in LDS
+            store_staged_c<BM, BN>(g, lds, m0, n0, tid);
+        }
         return;
     }
 
@@ -375,6 +409,34 @@ void k_gemm_nvfp4(GemmArgs g)
     // epilogue: register r of lane l holds C[row = l%32][col = 8*(r/4) +
     // 4*(l/32) + r%4] of each 32x32 tile
     float amax = 0.0f;                  // max |C| over this lane's stored outputs
+    if (!LORA && g.stage_ok) {
+        // bf16 tile into the (now idle) stage buffers, then all eight waves
+        // write whole rows with 16-byte stores
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            const int lrow = wm * 32 * TM + i * 32 + l32;
+            const bool rok = m0 + lrow < g.M;
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int lcol = wn * 32 * TN + j * 32 + 8 * q + 4 * half;
+                    const float v0 = acc[i][j][4 * q + 0] * scale, v1 = acc[i][j][4 * q + 1] * scale;
+                    const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
+                    if (rok && n0 + lcol < g.N)         // N % 8 == 0: the quad is in or out as a whole
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
+                    const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1, h2 = (__bf16)v2, h3 = (__bf16)v3;
+                    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    *reinterpret_cast<uint2 *>(lds + lrow * c_pitch(BN) + lcol * 2) = make_uint2(w0, w1);
+                }
+            }
+        }
+        __syncthreads();
+        store_staged_c<BM, BN>(g, lds, m0, n0, tid);
+    } else {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int row = m0 + wm * 32 * TM + i * 32 + l32;
@@ -419,6 +481,7 @@ void k_gemm_nvfp4(GemmArgs g)
                 }
             }
         }
+    }
     }
     if (g.c_amax) {
         // rounding to bf16 is monotone: the max of the stored values is the
@@ -492,6 +555,7 @@ hipError_t launch_gemm(const GemmOperand &a, const GemmOperand &b, int64_t m, in
     g.tiles_m = g.tiles_n = 0;
     const uintptr_t esz = cdtype == 1 ? 2 : 4;
     g.vec_ok = ((uintptr_t)c % (4 * esz) == 0) && (ldc % 4 == 0);
+    g.stage_ok = cdtype == 1 && (uintptr_t)c % 16 == 0 && ldc % 8 == 0 && n % 8 == 0;
     // candidate tiles (TM, TN); 256x256 needs more registers than a 2-wave/SIMD launch has
     const int cand[4][2] = {{3, 4}, {4, 3}, {2, 4}, {2, 2}};
     int pick = 0;
