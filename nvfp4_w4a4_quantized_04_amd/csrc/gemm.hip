@@ -199,10 +199,15 @@ __device__ __forceinline__ void store_staged_c(const GemmArgs &g, const uint8_t 
     }
 }
 
-template <int TM, int TN, bool KFULL, bool LORA>
+// EPI: 0 stores C straight from the accumulators, 1 stages a bf16 C tile
+// through LDS, 2 adds the LoRA branch first (then stores directly).  Separate
+// instances keep each epilogue's registers out of the others.
+template <int TM, int TN, bool KFULL, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_nvfp4(GemmArgs g)
 {
+    constexpr bool LORA = EPI == 2;
+    constexpr bool STAGED = EPI == 1;
     constexpr int BM = 64 * TM, BN = 64 * TN;
     constexpr int kStage = (BM + BN) * kLdsRow;
     constexpr int PD = kPrefetch;
@@ -307,7 +312,7 @@ void k_gemm_nvfp4(GemmArgs g)
             }
             __syncthreads();
         }
-        if (!LORA && g.stage_ok) {
+        if (STAGED) {
             __syncthreads();                              // the consumers staged C in LDS
             store_staged_c<BM, BN>(g, lds, m0, n0, tid);
         }
@@ -409,18 +414,24 @@ void k_gemm_nvfp4(GemmArgs g)
     // epilogue: register r of lane l holds C[row = l%32][col = 8*(r/4) +
     // 4*(l/32) + r%4] of each 32x32 tile
     float amax = 0.0f;                  // max |C| over this lane's stored outputs
-    if (!LORA && g.stage_ok) {
+    if (STAGED) {
         // bf16 tile into the (now idle) stage buffers, then all eight waves
-        // write whole rows with 16-byte stores
+        // write whole rows with 16-byte stores.  The lane's coordinates are
+        // recovered from the fragment offsets, which are live through the
+        // main loop anyway (keeping the thread index itself alive across the
+        // loop costs registers the loop does not have).
+        const int arow = a_frag[0] / kLdsRow;                  // wm*32*TM + l32
+        const int ehalf = (a_frag[0] - arow * kLdsRow) >> 4;
+        const int bcol0 = b_frag[0] / kLdsRow - BM - (arow & 31);   // wn*32*TN
 #pragma unroll
         for (int i = 0; i < TM; i++) {
-            const int lrow = wm * 32 * TM + i * 32 + l32;
+            const int lrow = arow + i * 32;
             const bool rok = m0 + lrow < g.M;
 #pragma unroll
             for (int j = 0; j < TN; j++) {
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const int lcol = wn * 32 * TN + j * 32 + 8 * q + 4 * half;
+                    const int lcol = bcol0 + j * 32 + 8 * q + 4 * ehalf;
                     const float v0 = acc[i][j][4 * q + 0] * scale, v1 = acc[i][j][4 * q + 1] * scale;
                     const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
                     if (rok && n0 + lcol < g.N)         // N % 8 == 0: the quad is in or out as a whole
@@ -435,7 +446,9 @@ void k_gemm_nvfp4(GemmArgs g)
             }
         }
         __syncthreads();
-        store_staged_c<BM, BN>(g, lds, m0, n0, tid);
+        // wave = 2*wm + wn, lane = 32*half + l32
+        const int ctid = ((arow / (32 * TM)) * 2 + bcol0 / (32 * TN)) * 64 + ehalf * 32 + (arow & 31);
+        store_staged_c<BM, BN>(g, lds, m0, n0, ctid);
     } else {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
@@ -489,7 +502,8 @@ void k_gemm_nvfp4(GemmArgs g)
         if (g.c_bf16)
             amax = (float)(__bf16)amax;
         amax = wave_max(amax);
-        if (lane == 0)
+        // lane index recomputed (mbcnt) rather than kept live across the main loop
+        if (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0)
             atomicMax(reinterpret_cast<unsigned int *>(g.c_amax), __float_as_uint(amax));
     }
 }
@@ -501,16 +515,21 @@ static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
     const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
     const bool kfull = g.K % kBK == 0;
-    if (g.lora_u) {
-        if (kfull)
-            k_gemm_nvfp4<TM, TN, true, true><<<(unsigned)grid, 512, 0, s>>>(g);
+    const int epi = g.lora_u ? 2 : g.stage_ok ? 1 : 0;
+    if (kfull) {
+        if (epi == 2)
+            k_gemm_nvfp4<TM, TN, true, 2><<<(unsigned)grid, 512, 0, s>>>(g);
+        else if (epi == 1)
+            k_gemm_nvfp4<TM, TN, true, 1><<<(unsigned)grid, 512, 0, s>>>(g);
         else
-            k_gemm_nvfp4<TM, TN, false, true><<<(unsigned)grid, 512, 0, s>>>(g);
+            k_gemm_nvfp4<TM, TN, true, 0><<<(unsigned)grid, 512, 0, s>>>(g);
     } else {
-        if (kfull)
-            k_gemm_nvfp4<TM, TN, true, false><<<(unsigned)grid, 512, 0, s>>>(g);
+        if (epi == 2)
+            k_gemm_nvfp4<TM, TN, false, 2><<<(unsigned)grid, 512, 0, s>>>(g);
+        else if (epi == 1)
+            k_gemm_nvfp4<TM, TN, false, 1><<<(unsigned)grid, 512, 0, s>>>(g);
         else
-            k_gemm_nvfp4<TM, TN, false, false><<<(unsigned)grid, 512, 0, s>>>(g);
+            k_gemm_nvfp4<TM, TN, false, 0><<<(unsigned)grid, 512, 0, s>>>(g);
     }
     return hipGetLastError();
 }
