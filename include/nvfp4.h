@@ -59,6 +59,11 @@
  *     aligned pointer and a leading dimension that is a multiple of 8
  *     elements; every other tensor (COL16 input, GEMM output, ...) only
  *     needs element alignment.  Leading dimensions are >= the row length.
+ *   - Sizes: every dimension below 2^31.  Entry points that run the GEMM
+ *     (nvfp4_gemm, nvfp4_linear, nvfp4_linear_lora, nvfp4_wgrad and the
+ *     DGRAD use of nvfp4_linear) also need each packed operand below 4 GiB
+ *     (rows * k / 2 < 2^32 for both A and B); larger calls return
+ *     NVFP4_ERR_SHAPE.
  *   - Numeric contract: inputs finite and amax == 0 or amax >= 2^-96;
  *     otherwise results are unspecified, but no call faults.
  */

@@ -18,6 +18,13 @@ inline bool dtype_ok(int d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
 inline bool rule_ok(int r) { return r == NVFP4_RULE_STATIC6 || r == NVFP4_RULE_4OVER6; }
 inline bool block_ok(int b) { return b == NVFP4_ROW16 || b == NVFP4_TILE16 || b == NVFP4_COL16; }
 inline bool dims_ok(int64_t r, int64_t c) { return r >= 0 && c >= 0 && r < kMaxDim && c < kMaxDim; }
+// The GEMM's producer waves address each packed operand ([rows][k/2] code
+// bytes) with 32-bit byte offsets: both operands must stay below 4 GiB.
+inline bool gemm_operands_fit(int64_t m, int64_t n, int64_t k)
+{
+    const int64_t lim = (int64_t)1 << 32;
+    return m * (k / 2) < lim && n * (k / 2) < lim;
+}
 
 nvfp4_status_t launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
 
@@ -156,7 +163,8 @@ nvfp4_status_t nvfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const
         return (a_scale_layout != 0 && a_scale_layout != 1) || (b_scale_layout != 0 && b_scale_layout != 1)
                    ? NVFP4_ERR_DTYPE
                    : NVFP4_ERR_SHAPE;
-    if (m < 0 || n < 0 || k < 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % 16 != 0 || ldc < n)
+    if (m < 0 || n < 0 || k < 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim || k % 16 != 0 || ldc < n ||
+        !gemm_operands_fit(m, n, k))
         return NVFP4_ERR_SHAPE;
     if (m > 0 && n > 0) {
         if (!c || !a_alpha || !b_alpha)
@@ -200,7 +208,7 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype) || !rule_ok(rule) ||
         (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
         return NVFP4_ERR_DTYPE;
-    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n ||
+    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n || !gemm_operands_fit(m, n, k) ||
         (w_scale_layout == NVFP4_SCALE_2D && n % 16 != 0))
         return NVFP4_ERR_SHAPE;
     if (!w_alpha || (m > 0 && n > 0 && !y) || (m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!w_codes || !w_scales)))
@@ -250,7 +258,7 @@ nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ld
         return NVFP4_ERR_ALIGN;
     if (!dtype_ok(y_dtype) || !rule_ok(rule) || (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
         return NVFP4_ERR_DTYPE;
-    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n ||
+    if (!dims_ok(m, k) || !dims_ok(n, 1) || k % 16 != 0 || ldx < k || ldy < n || !gemm_operands_fit(m, n, k) ||
         (w_scale_layout == NVFP4_SCALE_2D && n % 16 != 0))
         return NVFP4_ERR_SHAPE;
     if (!w_alpha || (m > 0 && n > 0 && !y) || (m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!w_codes || !w_scales)))
@@ -303,6 +311,7 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
     if (!dtype_ok(dtype) || !dtype_ok(dw_dtype) || !rule_ok(rule) || !signs_ok(rht_signs))
         return NVFP4_ERR_DTYPE;
     if (!dims_ok(tokens, n_out) || !dims_ok(k_in, 1) || tokens % 16 != 0 || lddy < n_out || ldx < k_in ||
+        !gemm_operands_fit(n_out, k_in, tokens) ||
         lddw < k_in)
         return NVFP4_ERR_SHAPE;
     if ((n_out > 0 && k_in > 0 && !dw) || (tokens > 0 && ((n_out > 0 && !dy) || (k_in > 0 && !x))))

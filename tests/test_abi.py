@@ -76,6 +76,11 @@ def test_gemm_and_linear_validation_without_gpu():
     assert g(*ok, 32, 32, 32, None, 0, 32, None, None) == 1
     assert g(*ok, 32, 32, 32, FAKE + 2, 0, 36, None, None) == 3       # fp32 C needs 4-byte alignment
     assert g(*ok, 32, 32, 32, FAKE, 0, 36, FAKE + 2, None) == 3        # amax output needs 4-byte alignment
+    # each packed operand below 4 GiB (32-bit offsets in the GEMM's producer waves)
+    assert g(*ok, 1 << 20, 32, 1 << 13, FAKE, 0, 32, None, None) == 2       # A: 2^20 rows x 2^12 bytes
+    assert g(*ok, 32, 1 << 20, 1 << 13, FAKE, 0, 1 << 20, None, None) == 2  # B
+    assert m.lib.nvfp4_linear(FAKE, 1, 1 << 20, 1 << 13, 1 << 13, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None,
+                              FAKE, 1 << 40, None) == 2
     lin = m.lib.nvfp4_linear
     assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None, FAKE, 10, None) == 5
     need = m.lib.nvfp4_linear_workspace_size(32, 64)
@@ -85,6 +90,7 @@ def test_gemm_and_linear_validation_without_gpu():
     assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, -1, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
     assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, 0x10000, FAKE, 0, 32, FAKE, 1 << 30, None) == 4  # signs
     assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, -2, FAKE, 0, 32, FAKE, 1 << 30, None) == 4
+    assert w(FAKE, FAKE, 1, 1 << 23, 1 << 10, 32, 1 << 10, 32, 1, -1, FAKE, 0, 32, FAKE, 1 << 40, None) == 2
     r = m.lib.nvfp4_quantize_col16_rht
     assert r(FAKE, 1, 32, 32, 32, 1, -1, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 4     # transform required
     assert r(FAKE, 1, 24, 32, 32, 1, 7, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2      # rows % 16
