@@ -66,7 +66,7 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 __host__ __device__ constexpr int lora_row_bytes(int r) { return 2 * r + 16; }
 
 template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f)
+__host__ __device__ __forceinline__ void static_for(F &&f)
 {
     if constexpr (B < E) {
         f(std::integral_constant<int, B>{});
@@ -199,15 +199,15 @@ __device__ __forceinline__ void store_staged_c(const GemmArgs &g, const uint8_t 
     }
 }
 
-// EPI: 0 stores C straight from the accumulators, 1 stages a bf16 C tile
-// through LDS, 2 adds the LoRA branch first (then stores directly).  Separate
-// instances keep each epilogue's registers out of the others.
+// EPI bit 0: stage a bf16 C tile through LDS (else store C straight from the
+// accumulators); bit 1: add the LoRA branch first.  Separate instances keep
+// each epilogue's registers out of the others.
 template <int TM, int TN, bool KFULL, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_nvfp4(GemmArgs g)
 {
-    constexpr bool LORA = EPI == 2;
-    constexpr bool STAGED = EPI == 1;
+    constexpr bool LORA = (EPI & 2) != 0;
+    constexpr bool STAGED = (EPI & 1) != 0;
     constexpr int BM = 64 * TM, BN = 64 * TN;
     constexpr int kStage = (BM + BN) * kLdsRow;
     constexpr int PD = kPrefetch;
@@ -313,6 +313,8 @@ void k_gemm_nvfp4(GemmArgs g)
             __syncthreads();
         }
         if (STAGED) {
+            if (LORA)
+                __syncthreads();                          // the consumers' reads of U and B are done
             __syncthreads();                              // the consumers staged C in LDS
             store_staged_c<BM, BN>(g, lds, m0, n0, tid);
         }
@@ -415,6 +417,8 @@ void k_gemm_nvfp4(GemmArgs g)
     // 4*(l/32) + r%4] of each 32x32 tile
     float amax = 0.0f;                  // max |C| over this lane's stored outputs
     if (STAGED) {
+        if (LORA)
+            __syncthreads();          // every wave has read its U and B fragments: LDS is free
         // bf16 tile into the (now idle) stage buffers, then all eight waves
         // write whole rows with 16-byte stores.  The lane's coordinates are
         // recovered from the fragment offsets, which are live through the
@@ -515,22 +519,16 @@ static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
     const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
     const bool kfull = g.K % kBK == 0;
-    const int epi = g.lora_u ? 2 : g.stage_ok ? 1 : 0;
-    if (kfull) {
-        if (epi == 2)
-            k_gemm_nvfp4<TM, TN, true, 2><<<(unsigned)grid, 512, 0, s>>>(g);
-        else if (epi == 1)
-            k_gemm_nvfp4<TM, TN, true, 1><<<(unsigned)grid, 512, 0, s>>>(g);
-        else
-            k_gemm_nvfp4<TM, TN, true, 0><<<(unsigned)grid, 512, 0, s>>>(g);
-    } else {
-        if (epi == 2)
-            k_gemm_nvfp4<TM, TN, false, 2><<<(unsigned)grid, 512, 0, s>>>(g);
-        else if (epi == 1)
-            k_gemm_nvfp4<TM, TN, false, 1><<<(unsigned)grid, 512, 0, s>>>(g);
-        else
-            k_gemm_nvfp4<TM, TN, false, 0><<<(unsigned)grid, 512, 0, s>>>(g);
-    }
+    const int epi = (g.lora_u ? 2 : 0) | (g.stage_ok ? 1 : 0);
+    static_for<0, 4>([&](auto e) {
+        constexpr int E = decltype(e)::value;
+        if (epi == E) {
+            if (kfull)
+                k_gemm_nvfp4<TM, TN, true, E><<<(unsigned)grid, 512, 0, s>>>(g);
+            else
+                k_gemm_nvfp4<TM, TN, false, E><<<(unsigned)grid, 512, 0, s>>>(g);
+        }
+    });
     return hipGetLastError();
 }
 
