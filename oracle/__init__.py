@@ -16,6 +16,26 @@ Parity status of each function (how it is pinned, see tests/test_oracle_*.py):
   dequantize                 pinned: exact products on representable inputs
   gemm_f64 / gemm_sampled    pinned: exact-rational sums, one-hot operands,
                              transposition symmetry
+  bf16_rne                   pinned: brute-force nearest-even over the two
+                             bf16 neighbours, ties included
+  transpose_tile16           pinned: involution, and quantize(x^T) equals the
+                             transpose on blocks whose tiles are exact
+  rht16                      pinned: integer inputs against the explicit
+                             (1/4) H16 D matrix product; fp32 error within
+                             the four-stage bound of the fp64 product; norm
+                             preserved; D H / 4 undoes it exactly on integers
+  quantize_col16_rht         pinned: COL16 quantization of the tensor
+                             transformed block by block with rht16
+  kv_smooth                  pinned: constant vectors give zero, shift
+                             invariance, mean within ulps of the fp64 mean
+  kv_quantize_smoothed       pinned: ROW16 quantization of kv_smooth's output
+  kv_window                  pinned: one whole part equals dequantize, parts
+                             concatenated in order, exact integer sums with
+                             the means, bf16 output = bf16_rne of fp32
+  lora_down_bf16             pinned: integer operands (exact dot products)
+                             against a brute-force bf16 rounding
+  linear_lora_f64            pinned: zero branch equals gemm_f64, one-hot
+                             branch adds exactly scale * U * B
   The fp32 evaluation order (readings R3/R4) is not fixed by the pages: where
   it differs from the exact-real reading (near ties) parity is unpinned and
   the rate is measured by ``quantize_exact_reading``.

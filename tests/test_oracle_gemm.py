@@ -157,6 +157,18 @@ def test_bf16_rounding_of_doubles():
     assert np.array_equal(got, np.array([_bf16_brute(v) for v in y], np.uint16))
 
 
+def test_bf16_rne_of_floats():
+    # fp32 -> bf16 (the comparison rounding of every bf16 output): brute force
+    # nearest-even over the two bf16 neighbours, ties included
+    rng = np.random.default_rng(53)
+    y = (rng.standard_normal(3000) * 10.0 ** rng.uniform(-20, 20, 3000)).astype(np.float32)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0 * 2.0 ** -100], np.float32)
+    y = np.concatenate([ties, y])
+    got = oracle.bf16_rne(y)
+    assert list(got[:3]) == [0x3F80, 0x3F82, 0xBF80]
+    assert np.array_equal(got, np.array([_bf16_brute(float(v)) for v in y], np.uint16))
+
+
 def test_lora_down_integer_closed_form():
     # small integers: every dot product is exact, U is its bf16 rounding
     rng = np.random.default_rng(51)

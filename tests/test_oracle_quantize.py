@@ -494,3 +494,32 @@ def test_kv_smooth_order_and_quantize():
     p, m2 = oracle.kv_quantize_smoothed(k)
     q = oracle.quantize(ks, ROW16, FOUR_OVER_SIX)
     assert np.array_equal(p.codes, q.codes) and np.array_equal(p.scales, q.scales) and np.array_equal(m, m2)
+
+
+def test_kv_window_pins():
+    # one whole part without means is the plain dequantization; parts are
+    # concatenated in order; the means are added once in fp32; bf16 output is
+    # the nearest-even rounding of the fp32 window
+    rng = np.random.default_rng(42)
+    k1 = rng.standard_normal((40, 32)).astype(np.float32)
+    k2 = rng.standard_normal((24, 32)).astype(np.float32)
+    p1 = oracle.quantize(k1, ROW16, FOUR_OVER_SIX)
+    p2 = oracle.quantize(k2, ROW16, FOUR_OVER_SIX)
+    d1, d2 = oracle.dequantize(p1), oracle.dequantize(p2)
+    assert np.array_equal(oracle.kv_window([(p1, None, 0, 40)], out_bf16=False), d1)
+    w = oracle.kv_window([(p2, None, 3, 5), (p1, None, 10, 7)], out_bf16=False)
+    assert np.array_equal(w, np.concatenate([d2[3:8], d1[10:17]]))
+    # means that are powers of two far above the values: the add is exact
+    # only in the high bits, so compare with the one-rounding fp32 sum
+    means = (2.0 ** rng.integers(-3, 4, 40)).astype(np.float32)
+    w = oracle.kv_window([(p1, means, 2, 30)], out_bf16=False)
+    assert np.array_equal(w, (d1[2:32] + means[2:32, None]).astype(np.float32))
+    # values q * 448 with a block max of 2688: alpha = 1 and s = 448 exactly,
+    # so every decoded value and every sum with a small integer mean is exact
+    vals = np.tile(np.array([1, 2, 3, 4, 6, 0, -1, -6], np.float32) * 448, (8, 4))
+    q = oracle.quantize(vals, ROW16, FOUR_OVER_SIX)
+    m8 = np.arange(8, dtype=np.float32)
+    w = oracle.kv_window([(q, m8, 0, 8)], out_bf16=False)
+    assert np.array_equal(w, vals + m8[:, None])
+    wb = oracle.kv_window([(p2, None, 3, 5), (p1, means, 10, 7)], out_bf16=True)
+    assert np.array_equal(wb, oracle.bf16_rne(oracle.kv_window([(p2, None, 3, 5), (p1, means, 10, 7)], out_bf16=False)))
