@@ -178,7 +178,8 @@ def test_dgrad(m, n, k):
     assert rel_frobenius(host_bits(dx), ref2) <= GEMM_RTOL
 
 
-@pytest.mark.parametrize("m,n,k,r", [(300, 384, 512, 128), (17, 64, 48, 32), (1000, 1040, 272, 64)])
+@pytest.mark.parametrize("m,n,k,r", [(300, 384, 512, 128), (17, 64, 48, 32), (1000, 1040, 272, 64),
+                                     (33, 257, 96, 32)])
 def test_linear_lora(m, n, k, r):
     """W4A4 linear + BF16 LoRA branch: U = bf16(x A^T) checked against the
     exact sums (check_lora_u), and y against the fp64 reference built on the
@@ -189,7 +190,8 @@ def test_linear_lora(m, n, k, r):
     w = workloads.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     la = workloads.f32_to_bf16_bits((rng.standard_normal((r, k)) / np.sqrt(k)).astype(np.float32))
     lb = workloads.f32_to_bf16_bits((rng.standard_normal((n, r)) * 0.02).astype(np.float32))
-    W = oracle.quantize(w, oracle.TILE16, 1)
+    # N % 16 != 0 takes a 1x16-block weight (and N % 8 != 0 the unstaged bf16 epilogue)
+    W = oracle.quantize(w, oracle.TILE16 if n % 16 == 0 else oracle.ROW16, 1)
     Wd = packed_to_device(W)
     scale = 0.75
     y, u = nv.linear_lora(dev_from_host(x), Wd, dev_from_host(la), dev_from_host(lb), scale, torch.float32)
