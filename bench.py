@@ -45,8 +45,8 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
 # counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
 # counters read for a plain 256 MiB device copy.  They hold for the GEMM
 # source they were taken with only: null once gemm.hip has changed.
-GEMM_TRAFFIC = {"gemm_src_sha256": "0a9ea609045094dc48de5e2e8fc4d464bd0c143506e0e92aa6984d0419f67c6b",
-                "bytes_per_launch": 140032815}
+GEMM_TRAFFIC = {"gemm_src_sha256": "c093437f501103807fd79fac36b9d89d597f3a4dd9785b3b5aabfcecf4e36d2d",
+                "bytes_per_launch": 140021466}
 
 
 def gemm_traffic():
