@@ -19,11 +19,14 @@ inline bool rule_ok(int r) { return r == NVFP4_RULE_STATIC6 || r == NVFP4_RULE_4
 inline bool block_ok(int b) { return b == NVFP4_ROW16 || b == NVFP4_TILE16 || b == NVFP4_COL16; }
 inline bool dims_ok(int64_t r, int64_t c) { return r >= 0 && c >= 0 && r < kMaxDim && c < kMaxDim; }
 // The GEMM's producer waves address each packed operand ([rows][k/2] code
-// bytes) with 32-bit byte offsets: both operands must stay below 4 GiB.
+// bytes) with 32-bit byte offsets: both operands must stay below 4 GiB.  Its
+// launch has 512 threads per output tile (at least 128 x 128) and a dispatch
+// counts work-items in 32 bits: fewer than 2^23 tiles of 128 x 128.
 inline bool gemm_operands_fit(int64_t m, int64_t n, int64_t k)
 {
     const int64_t lim = (int64_t)1 << 32;
-    return m * (k / 2) < lim && n * (k / 2) < lim;
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    return m * (k / 2) < lim && n * (k / 2) < lim && tiles < ((int64_t)1 << 23);
 }
 
 nvfp4_status_t launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }

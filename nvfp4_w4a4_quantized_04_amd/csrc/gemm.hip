@@ -528,6 +528,8 @@ static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
     g.tiles_m = (g.M + 64 * TM - 1) / (64 * TM);
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
     const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
+    if (grid * 512 > (int64_t)0xFFFFFFFF)
+        return hipErrorInvalidConfiguration;   // a dispatch counts its work-items in 32 bits
     const bool kfull = g.K % kBK == 0;
     const int epi = (g.lora_u ? 2 : 0) | (g.stage_ok ? 1 : 0);
     static_for<0, 4>([&](auto e) {

@@ -79,6 +79,7 @@ def test_gemm_and_linear_validation_without_gpu():
     # each packed operand below 4 GiB (32-bit offsets in the GEMM's producer waves)
     assert g(*ok, 1 << 20, 32, 1 << 13, FAKE, 0, 32, None, None) == 2       # A: 2^20 rows x 2^12 bytes
     assert g(*ok, 32, 1 << 20, 1 << 13, FAKE, 0, 1 << 20, None, None) == 2  # B
+    assert g(*ok, 1 << 27, 1 << 23, 16, FAKE, 0, 1 << 23, None, None) == 2  # 2^23 tiles of 128 x 128
     assert m.lib.nvfp4_linear(FAKE, 1, 1 << 20, 1 << 13, 1 << 13, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None,
                               FAKE, 1 << 40, None) == 2
     lin = m.lib.nvfp4_linear
