@@ -133,9 +133,19 @@ def _out_dtype_code(d) -> int:
 
 
 def _need_gpu(*ts):
+    """Device tensors on the current device: the library enqueues on the
+    current device's current stream and dereferences the pointers there."""
+    cur = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("NVFP4 kernels need device tensors (no CPU fallback)")
+        if cur is None:
+            cur = torch.cuda.current_device()
+        if t.device.index != cur:
+            raise ValueError(f"tensor on {t.device} but the current device is cuda:{cur} "
+                             "(call torch.cuda.set_device first)")
 
 
 @dataclass
@@ -195,6 +205,7 @@ def quantize(x: torch.Tensor, block="row16", rule="4over6", amax: torch.Tensor |
     if workspace is None and amax is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
     wsz = 0 if workspace is None else workspace.numel()
+    _need_gpu(out.codes, out.scales, out.alpha, workspace)
     _check("nvfp4_quantize", lib.nvfp4_quantize(
         _ptr(x), _dtype_code(x), rows, cols, x.stride(0), b, _rule(rule), _ptr(amax),
         _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), wsz, _stream()))
@@ -206,6 +217,7 @@ def dequantize(t: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = N
     _need_gpu(t.codes)
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    _need_gpu(t.scales, t.alpha, out)
     _check("nvfp4_dequantize", lib.nvfp4_dequantize(
         _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, t.block,
         _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
@@ -223,6 +235,7 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Ten
     _need_gpu(ca, cb)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=ca.device)
+    _need_gpu(sa, aa, sb, ab, out, amax_out)
     _check("nvfp4_gemm", lib.nvfp4_gemm(
         _ptr(ca), _ptr(sa), _ptr(aa), la, _ptr(cb), _ptr(sb), _ptr(ab), lb, m, n, k,
         _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _stream()))
@@ -242,6 +255,7 @@ def kv_quantize(kv: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
         out = empty_packed(vectors, d, ROW16, kv.device)
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(vectors, d), dtype=torch.uint8, device=kv.device)
+    _need_gpu(amax, out.codes, out.scales, out.alpha, workspace)
     _check("nvfp4_kv_quantize", lib.nvfp4_kv_quantize(
         _ptr(kv), _dtype_code(kv), vectors, d, _rule(rule), _ptr(amax), _ptr(out.codes), _ptr(out.scales),
         _ptr(out.alpha), _ptr(workspace), workspace.numel(), _stream()))
@@ -268,6 +282,7 @@ def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4ove
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
     if workspace is None:
         workspace = linear_workspace(m, k, x.device)
+    _need_gpu(cw, sw, aw, out, amax_out, workspace)
     _check("nvfp4_linear", lib.nvfp4_linear(
         _ptr(x), _dtype_code(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n,
         _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _ptr(workspace), workspace.numel(),
@@ -293,6 +308,7 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4ove
         out = torch.empty((n, k), dtype=out_dtype, device=x.device)
     if workspace is None:
         workspace = wgrad_workspace(t, n, k, x.device)
+    _need_gpu(out, workspace)
     _check("nvfp4_wgrad", lib.nvfp4_wgrad(
         _ptr(dy), _ptr(x), _dtype_code(x), t, n, k, dy.stride(0), x.stride(0), _rule(rule),
         -1 if rht_signs is None else int(rht_signs), _ptr(out), _out_dtype_code(out.dtype), out.stride(0),
@@ -307,6 +323,7 @@ def transpose_tile16(t: NVFP4Tensor, out: NVFP4Tensor | None = None) -> NVFP4Ten
     _need_gpu(t.codes)
     if out is None:
         out = empty_packed(t.cols, t.rows, TILE16, t.codes.device)
+    _need_gpu(t.scales, t.alpha, out.codes, out.scales, out.alpha)
     _check("nvfp4_transpose_tile16", lib.nvfp4_transpose_tile16(
         _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, _ptr(out.codes), _ptr(out.scales),
         _ptr(out.alpha), _stream()))
@@ -333,6 +350,7 @@ def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.T
         out = empty_packed(rows, cols, COL16, x.device)
     if workspace is None and amax is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
+    _need_gpu(out.codes, out.scales, out.alpha, workspace)
     _check("nvfp4_quantize_col16_rht", lib.nvfp4_quantize_col16_rht(
         _ptr(x), _dtype_code(x), rows, cols, x.stride(0), _rule(rule), int(signs), _ptr(amax), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), 0 if workspace is None else workspace.numel(),
@@ -355,6 +373,7 @@ def kv_quantize_smoothed(k: torch.Tensor, rule="4over6", out: NVFP4Tensor | None
         means = torch.empty(v, dtype=torch.float32, device=k.device)
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_kv_smooth_workspace_size(v, d), dtype=torch.uint8, device=k.device)
+    _need_gpu(out.codes, out.scales, out.alpha, means, workspace)
     _check("nvfp4_kv_quantize_smoothed", lib.nvfp4_kv_quantize_smoothed(
         _ptr(k), _dtype_code(k), v, d, _rule(rule), _ptr(out.codes), _ptr(out.scales), _ptr(out.alpha),
         _ptr(means), _ptr(workspace), workspace.numel(), _stream()))
@@ -378,10 +397,11 @@ def kv_dequantize_window(parts, out_dtype=torch.bfloat16, out: torch.Tensor | No
             raise ValueError("segments must be ROW16 chunks of one head_dim")
         if first < 0 or count < 0 or first + count > t.rows:
             raise ValueError("segment rows out of range")
-        _need_gpu(t.codes, means)
+        _need_gpu(t.codes, t.scales, t.alpha, means)
         segs[i] = KvSegment(_ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), _ptr(means), int(first), int(count))
     if out is None:
         out = torch.empty((rows, d), dtype=out_dtype, device=parts[0][0].codes.device)
+    _need_gpu(out)
     _check("nvfp4_kv_dequantize_window", lib.nvfp4_kv_dequantize_window(
         segs, len(parts), d, _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
     return out
@@ -437,6 +457,7 @@ def linear_lora(x: torch.Tensor, w: NVFP4Tensor, lora_a: torch.Tensor, lora_b: t
         u = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_linear_lora_workspace_size(m, k, r), dtype=torch.uint8, device=x.device)
+    _need_gpu(cw, sw, aw, u, out, amax_out, workspace)
     _check("nvfp4_linear_lora", lib.nvfp4_linear_lora(
         _ptr(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n, _ptr(lora_a), _ptr(lora_b), r,
         float(lora_scale), _ptr(u), _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out),

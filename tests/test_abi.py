@@ -161,3 +161,6 @@ def test_no_cpu_fallback():
     import nvfp4_w4a4_quantized_04_amd as m
     with pytest.raises(ValueError):
         m.quantize(torch.zeros(16, 16))
+    # every tensor the binding hands to the library must be a device tensor
+    with pytest.raises(ValueError):
+        m._need_gpu(None, torch.zeros(4))
