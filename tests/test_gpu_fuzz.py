@@ -1,0 +1,106 @@
+"""Seeded fuzz of the GPU path against the CPU oracle: random shapes (odd M,
+K any multiple of 16, N any multiple of 16), input dtypes, rules, weight block
+kinds and data mixes (normal, outlier-heavy, denormal-heavy rows, rows of
+mixed magnitude, all-zero rows).  Each case checks the activation and weight
+quantizers bit-exact, the GEMM (fp32 output) within the relative Frobenius
+bound, bf16 output as the nearest-even rounding of the fp32 output, and the
+fused linear against quantize-then-GEMM of the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, dev_from_host, host_bits, packed_to_device,
+                               rel_frobenius)
+
+pytestmark = pytest.mark.gpu
+
+nv = pytest.importorskip("nvfp4_w4a4_quantized_04_amd")
+
+MIXES = ("normal", "outliers", "denormal_rows", "row_magnitudes", "zero_rows")
+
+
+def _data(g, shape, mix):
+    x = g.standard_normal(shape)
+    if mix == "outliers":
+        n = max(1, x.size // 200)
+        idx = g.choice(x.size, n, replace=False)
+        x.flat[idx] *= 50.0
+    elif mix == "denormal_rows":
+        rows = g.choice(shape[0], max(1, shape[0] // 4), replace=False)
+        x[rows] *= 2.0 ** -130                       # fp32 / bf16 subnormals next to normal rows
+    elif mix == "row_magnitudes":
+        x *= 10.0 ** g.uniform(-3, 3, (shape[0], 1))
+    elif mix == "zero_rows":
+        rows = g.choice(shape[0], max(1, shape[0] // 3), replace=False)
+        x[rows] = 0.0
+    return x.astype(np.float32)
+
+
+def _cases(n=24, seed=2024):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        m = int(g.integers(1, 600))
+        k = 16 * int(g.integers(1, 80))
+        nn = 16 * int(g.integers(1, 48))
+        out.append((i, m, nn, k, MIXES[i % len(MIXES)], bool(g.integers(0, 2)), int(g.integers(0, 2)),
+                    bool(g.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"c{c[0]}_m{c[1]}_n{c[2]}_k{c[3]}_{c[4]}")
+def test_fuzz_quantize_gemm_linear(case):
+    i, m, n, k, mix, bf16_in, rule, tile_w = case
+    print(f"[case] fuzz {case}", flush=True)
+    g = np.random.default_rng(1000 + i)
+    x = _data(g, (m, k), mix)
+    w = (_data(g, (n, k), "normal" if mix == "zero_rows" else mix) * 0.02).astype(np.float32)
+    if bf16_in:
+        x = workloads.f32_to_bf16_bits(x)
+        w = workloads.f32_to_bf16_bits(w)
+    wblock = oracle.TILE16 if tile_w else oracle.ROW16
+    A = oracle.quantize(x, oracle.ROW16, rule)
+    W = oracle.quantize(w, wblock, rule)
+    xd = dev_from_host(x)
+    ga = nv.quantize(xd, "row16", rule)
+    gw = nv.quantize(dev_from_host(w), "tile16" if tile_w else "row16", rule)
+    torch.cuda.synchronize()
+    assert_packed_equal(ga, A, f"A {case}")
+    assert_packed_equal(gw, W, f"W {case}")
+    ref = oracle.gemm_f64(A, W)
+    c32 = nv.gemm(ga, gw, torch.float32)
+    c16 = nv.gemm(ga, gw, torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = host_bits(c32)
+    if np.any(ref):
+        assert rel_frobenius(g32, ref) <= GEMM_RTOL
+    else:
+        assert not np.any(g32)
+    assert np.array_equal(host_bits(c16), oracle.bf16_rne(g32))
+    # the fused linear (activation quantized inside the call) against the same product
+    y = nv.linear(xd, packed_to_device(W), torch.float32, rule=rule)
+    torch.cuda.synchronize()
+    gy = host_bits(y)
+    if np.any(ref):
+        assert rel_frobenius(gy, ref) <= GEMM_RTOL
+    else:
+        assert not np.any(gy)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_col16(seed):
+    """COL16 (weight-gradient operands): rows a multiple of 16, any column count."""
+    g = np.random.default_rng(3000 + seed)
+    rows = 16 * int(g.integers(1, 40))
+    cols = int(g.integers(1, 300))
+    x = _data(g, (rows, cols), MIXES[seed % len(MIXES)])
+    if seed % 2:
+        x = workloads.f32_to_bf16_bits(x)
+    rule = seed % 2
+    print(f"[case] fuzz col16 {rows}x{cols} seed={seed}", flush=True)
+    ref = oracle.quantize(x, oracle.COL16, rule)
+    got = nv.quantize(dev_from_host(x), "col16", rule)
+    torch.cuda.synchronize()
+    assert_packed_equal(got, ref, f"col16 {rows}x{cols}")
