@@ -295,29 +295,29 @@ void k_gemm_nvfp4(GemmArgs g)
             constexpr int kBatch = 8;                       // loads in flight per thread
             for (int q0 = ptid; q0 < total; q0 += 256 * kBatch) {
                 uint4 v[kBatch];
+                // every load unconditional (an index past the end re-reads the
+                // last chunk): a load under a branch would be waited for
+                // before the next one is issued
 #pragma unroll
                 for (int u = 0; u < kBatch; u++) {
-                    const int q = q0 + u * 256;
-                    if (q < total) {
-                        const int row = q / vpr, cv = q - row * vpr;
-                        const uint16_t *src;
-                        if (row < BM) {
-                            const int gr = m0 + row < g.M ? m0 + row : g.M - 1;
-                            src = g.lora_u + (int64_t)gr * g.lora_r;
-                        } else {
-                            const int gr = n0 + row - BM < g.N ? n0 + row - BM : g.N - 1;
-                            src = g.lora_b + (int64_t)gr * g.lora_r;
-                        }
-                        v[u] = *reinterpret_cast<const uint4 *>(src + cv * 8);
+                    const int q = q0 + u * 256 < total ? q0 + u * 256 : total - 1;
+                    const int row = q / vpr, cv = q - row * vpr;
+                    const uint16_t *src;
+                    if (row < BM) {
+                        const int gr = m0 + row < g.M ? m0 + row : g.M - 1;
+                        src = g.lora_u + (int64_t)gr * g.lora_r;
+                    } else {
+                        const int gr = n0 + row - BM < g.N ? n0 + row - BM : g.N - 1;
+                        src = g.lora_b + (int64_t)gr * g.lora_r;
                     }
+                    v[u] = *reinterpret_cast<const uint4 *>(src + cv * 8);
                 }
 #pragma unroll
                 for (int u = 0; u < kBatch; u++) {
-                    const int q = q0 + u * 256;
-                    if (q < total) {
-                        const int row = q / vpr, cv = q - row * vpr;
-                        *reinterpret_cast<uint4 *>(lds + row * pr + cv * 16) = v[u];
-                    }
+                    // past the end: the last chunk again (same value, same place)
+                    const int q = q0 + u * 256 < total ? q0 + u * 256 : total - 1;
+                    const int row = q / vpr, cv = q - row * vpr;
+                    *reinterpret_cast<uint4 *>(lds + row * pr + cv * 16) = v[u];
                 }
             }
             __syncthreads();

@@ -33,41 +33,48 @@ __global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict
     const int chunks = nrows * 8;                  // 16-byte chunks per 64-k step
     float16v acc = float16v{};
     const bool active = wave * 32 < r;
-    auto fetch = [&](int k0, uint4 (&v)[5]) {
+    // Every load is issued unconditionally (a load under a branch is waited
+    // for before the next one goes out): a chunk index past the end re-reads
+    // the last chunk, a k past the slice reads column 0 of the same row, and
+    // the bits of `ok` say which chunks lie inside the slice (the rest are
+    // staged as zero).
+    auto fetch = [&](int k0, uint4 (&v)[5]) -> unsigned {
+        unsigned ok = 0;
 #pragma unroll
         for (int u = 0; u < 5; u++) {
-            const int q = tid + u * 256;
-            v[u] = make_uint4(0, 0, 0, 0);
-            if (q < chunks) {
-                const int row = q >> 3, c = q & 7;
-                const int k = k0 + c * 8;
-                if (k < ke) {
-                    const uint16_t *src = row < 32 ? x + (int64_t)(m0 + row < M ? m0 + row : M - 1) * ldx
-                                                   : a + (int64_t)(row - 32) * K;
-                    v[u] = *reinterpret_cast<const uint4 *>(src + k);
-                }
-            }
+            const int q = tid + u * 256 < chunks ? tid + u * 256 : chunks - 1;
+            const int row = q >> 3, c = q & 7;
+            const int k = k0 + c * 8;
+            ok |= (unsigned)(k < ke) << u;                // of the clamped chunk: a repeat stores the same value
+            const uint16_t *src = row < 32 ? x + (int64_t)(m0 + row < M ? m0 + row : M - 1) * ldx
+                                           : a + (int64_t)(row - 32) * K;
+            v[u] = *reinterpret_cast<const uint4 *>(src + (k < ke ? k : 0));
         }
+        return ok;
     };
-    auto stash = [&](uint8_t *buf, const uint4 (&v)[5]) {
+    auto stash = [&](uint8_t *buf, const uint4 (&v)[5], unsigned ok) {
 #pragma unroll
         for (int u = 0; u < 5; u++) {
-            const int q = tid + u * 256;
-            if (q < chunks)
-                *reinterpret_cast<uint4 *>(buf + (q >> 3) * kLoraRowB + (q & 7) * 16) = v[u];
+            const int q = tid + u * 256 < chunks ? tid + u * 256 : chunks - 1;
+            uint4 w = v[u];
+            if (!((ok >> u) & 1))
+                w = make_uint4(0, 0, 0, 0);
+            // past the end: the last chunk again (same value, same place)
+            *reinterpret_cast<uint4 *>(buf + (q >> 3) * kLoraRowB + (q & 7) * 16) = w;
         }
     };
     uint4 v[5];
+    unsigned ok = 0;
     int buf = 0;
     if (kb < ke) {
-        fetch(kb, v);
-        stash(lds[0], v);
+        ok = fetch(kb, v);
+        stash(lds[0], v, ok);
     }
     __syncthreads();
     for (int k0 = kb; k0 < ke; k0 += 64) {
         const bool more = k0 + 64 < ke;
         if (more)
-            fetch(k0 + 64, v);                     // in flight under this step's MFMAs
+            ok = fetch(k0 + 64, v);                // in flight under this step's MFMAs
         if (active) {
             const uint8_t *st = lds[buf];
 #pragma unroll
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict
             }
         }
         if (more)
-            stash(lds[buf ^ 1], v);
+            stash(lds[buf ^ 1], v, ok);
         __syncthreads();
         buf ^= 1;
     }
