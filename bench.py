@@ -8,6 +8,10 @@ with fp32 accumulation and bf16 output -- one call of nvfp4_linear.
 device memory, three rotating input/weight sets.
 
 The same JSON line also carries
+  step_ms_events  p10 / median / p90 of the per-step GPU times (events
+                recorded between the timed steps);
+  gpu_state     rocm-smi clocks and power read while the step runs (untimed),
+                the device name and a SHA-256 stamp of the library sources;
   roofline      the GEMM kernel alone, timed with HIP events on its stream,
                 against the fp16 MFMA peak (its operands are exact fp16);
   kv            NVFP4 KV-cache quantize and dequantize of K and V bf16
@@ -119,11 +123,59 @@ def bench_linear(nv, sets, steps, warmup):
         if i % 20 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # one event after each step (a marker on the stream, no sync): the gaps
+    # between consecutive events are the per-step GPU times
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(steps):
         step(i)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    q = lambda f: per[min(steps - 1, int(f * steps))]
+    return ms, {"p10": round(q(0.1), 5), "median": round(q(0.5), 5), "p90": round(q(0.9), 5)}
+
+
+def gpu_state_under_load(step, seconds=2.0):
+    """rocm-smi's clock and power readings taken while the step runs back to
+    back (untimed), plus a stamp of the library sources."""
+    import glob
+    import hashlib
+    import subprocess
+    import threading
+    import torch
+    out = {}
+
+    def sample():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                               text=True, timeout=20)
+            out["rocm_smi"] = json.loads(r.stdout) if r.returncode == 0 else None
+        except Exception:
+            out["rocm_smi"] = None
+
+    th = threading.Thread(target=sample)
+    t_end = time.perf_counter() + seconds
+    i = 0
+    th.start()
+    while time.perf_counter() < t_end or th.is_alive():
+        step(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
+        if time.perf_counter() > t_end + 25:
+            break
+    torch.cuda.synchronize()
+    th.join(timeout=1)
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "nvfp4_w4a4_quantized_04_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    out["device"] = torch.cuda.get_device_name(0)
+    out["csrc_sha256"] = h.hexdigest()
+    return out
 
 
 def bench_gemm_kernel(nv, sets, iters):
@@ -264,7 +316,7 @@ def bench_extra(nv, workloads, iters):
                             "ffn_down_m2640_k14336_n3072": (2640, 14336, 3072),
                             "train_fwd_m32768_k3072_n3072": (32768, 3072, 3072)}.items():
         sets = linear_sets(nv, workloads, m, k, n, 2, 30)
-        ms = bench_linear(nv, sets, iters, 3)
+        ms, _ = bench_linear(nv, sets, iters, 3)
         out[name] = {"ms": round(ms, 4), "TFLOPs": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)}
         del sets
         torch.cuda.empty_cache()
@@ -417,9 +469,17 @@ def main():
         log("[bench] preparing QKV projection inputs")
         sets = linear_sets(nv, workloads, m, k, n, 3, 2)
         log("[bench] timing the fused linear")
-        ms = bench_linear(nv, sets, args.steps, args.warmup)
+        ms, dist = bench_linear(nv, sets, args.steps, args.warmup)
         value = flops / (ms * 1e-3) / 1e12
         log(f"[bench] linear {ms:.4f} ms/step, {value:.1f} TFLOP/s")
+        result["step_ms_events"] = dist
+
+        def step(i):
+            x, w, y, ws = sets[i % len(sets)]
+            nv.linear(x, w, torch.bfloat16, out=y, workspace=ws)
+
+        log("[bench] clocks and power under load (untimed)")
+        result["gpu_state"] = gpu_state_under_load(step)
         log("[bench] timing the GEMM kernel alone")
         gms = bench_gemm_kernel(nv, sets, max(50, args.steps // 2))
         achieved = flops / (gms * 1e-3) / 1e12
