@@ -10,8 +10,9 @@ device memory, three rotating input/weight sets.
 The same JSON line also carries
   step_ms_events  p10 / median / p90 of the per-step GPU times (events
                 recorded between the timed steps);
-  gpu_state     rocm-smi clocks and power read while the step runs (untimed),
-                the device name and a SHA-256 stamp of the library sources;
+  gpu_state     clock levels and board power (sysfs) read while the step
+                runs (untimed), the device name and a SHA-256 stamp of the
+                library sources;
   roofline      the GEMM kernel alone, timed with HIP events on its stream,
                 against the fp16 MFMA peak (its operands are exact fp16);
   kv            NVFP4 KV-cache quantize and dequantize of K and V bf16
@@ -49,8 +50,8 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
 # counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
 # counters read for a plain 256 MiB device copy.  They hold for the GEMM
 # source they were taken with only: null once gemm.hip has changed.
-GEMM_TRAFFIC = {"gemm_src_sha256": "c093437f501103807fd79fac36b9d89d597f3a4dd9785b3b5aabfcecf4e36d2d",
-                "bytes_per_launch": 140021466}
+GEMM_TRAFFIC = {"gemm_src_sha256": "27f763b7e8e99d91cc6181c4646c7cd8c8b64c6e66fb8e6426711a0414d00f01",
+                "bytes_per_launch": 140017664}
 
 
 def gemm_traffic():
@@ -138,23 +139,46 @@ def bench_linear(nv, sets, steps, warmup):
     return ms, {"p10": round(q(0.1), 5), "median": round(q(0.5), 5), "p90": round(q(0.9), 5)}
 
 
+def read_gpu_clocks():
+    """Current shader/memory clock levels and board power from sysfs (the
+    level marked '*' in pp_dpm_sclk / pp_dpm_mclk, hwmon power in W).  Plain
+    file reads: no tool is started."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        info = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+                info[name] = cur[0] if cur else None
+            except OSError:
+                pass
+        for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            for pname in ("power1_average", "power1_input"):
+                try:
+                    with open(os.path.join(hw, pname)) as f:
+                        info[pname + "_W"] = int(f.read().strip()) / 1e6
+                except (OSError, ValueError):
+                    pass
+        if info:
+            out[os.path.basename(os.path.dirname(dev))] = info
+    return out or None
+
+
 def gpu_state_under_load(step, seconds=2.0):
-    """rocm-smi's clock and power readings taken while the step runs back to
-    back (untimed), plus a stamp of the library sources."""
+    """Clock levels and power read from sysfs halfway through `seconds` of the
+    step running back to back (untimed), plus a stamp of the library
+    sources."""
     import glob
     import hashlib
-    import subprocess
     import threading
     import torch
     out = {}
 
     def sample():
-        try:
-            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
-                               text=True, timeout=20)
-            out["rocm_smi"] = json.loads(r.stdout) if r.returncode == 0 else None
-        except Exception:
-            out["rocm_smi"] = None
+        time.sleep(seconds / 2)
+        out["clocks"] = read_gpu_clocks()
 
     th = threading.Thread(target=sample)
     t_end = time.perf_counter() + seconds
@@ -165,7 +189,7 @@ def gpu_state_under_load(step, seconds=2.0):
         i += 1
         if i % 20 == 0:
             torch.cuda.synchronize()
-        if time.perf_counter() > t_end + 25:
+        if time.perf_counter() > t_end + 5:
             break
     torch.cuda.synchronize()
     th.join(timeout=1)
@@ -478,7 +502,7 @@ def main():
             x, w, y, ws = sets[i % len(sets)]
             nv.linear(x, w, torch.bfloat16, out=y, workspace=ws)
 
-        log("[bench] clocks and power under load (untimed)")
+        log("[bench] clock levels and power under load (untimed)")
         result["gpu_state"] = gpu_state_under_load(step)
         log("[bench] timing the GEMM kernel alone")
         gms = bench_gemm_kernel(nv, sets, max(50, args.steps // 2))
