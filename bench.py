@@ -23,7 +23,11 @@ The same JSON line also carries
                 gradient), and for context the vendor library's dense
                 fp16/bf16 GEMM on the QKV shape;
   cpu_baseline  the CPU oracle (fp32 quantizer, fp64 GEMM) on the full QKV
-                step on the host cores.
+                step on the host cores;
+  parity        the oracle's results of that leg against the library's on
+                the same seeded inputs (the first timed input set): codes,
+                scales and alpha bit-exact, fp32 output within relative
+                Frobenius 1e-5, bf16 output = RNE of the fp32 one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--parts qkv,kv,extra,cpu]
        python bench.py --copy-calibration   (a plain 256 MiB device copy, for
@@ -421,9 +425,38 @@ def bench_extra(nv, workloads, iters):
     return out
 
 
-def cpu_baseline(workloads, m, k, n):
+def gpu_outputs_for_parity(nv, workloads):
+    """The library's results on the first timed QKV input set (seed 2, full
+    size), copied to the host: the quantized activation and weight, and the
+    fused linear's fp32 and bf16 outputs."""
+    import numpy as np
+    import torch
+    c = workloads.config2()
+    x = dev_bf16(c["x"])
+    w = nv.quantize(dev_bf16(c["w"]), "tile16", "4over6")
+    a = nv.quantize(x, "row16", "4over6")
+    y32 = nv.linear(x, w, torch.float32)
+    y16 = nv.linear(x, w, torch.bfloat16)
+    torch.cuda.synchronize()
+
+    def packed(t):
+        return (t.codes.cpu().numpy(), t.scales.cpu().numpy(), np.float32(t.alpha.cpu().numpy()[0]))
+
+    out = {"a": packed(a), "w": packed(w), "y32": y32.cpu().numpy(),
+           "y16": y16.cpu().view(torch.int16).numpy().view(np.uint16)}
+    del x, w, a, y32, y16
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(workloads, m, k, n, gpu=None):
     """The oracle (fp32 quantizer, fp64 GEMM, OpenMP) on the full QKV step,
-    repeated until about 10 s of host time have passed (at most 8 steps)."""
+    repeated until about 10 s of host time have passed (at most 8 steps).
+    With `gpu` (gpu_outputs_for_parity on the same seeded inputs) the oracle's
+    results also check the library's at full size: codes, scale bytes and
+    alpha bit for bit, the fp32 output within relative Frobenius 1e-5, and the
+    bf16 output equal to the round-to-nearest-even of the fp32 one."""
+    import numpy as np
     import oracle
     c = workloads.config2()
     W = oracle.quantize(c["w"], oracle.TILE16, oracle.FOUR_OVER_SIX)     # offline, untimed
@@ -431,13 +464,31 @@ def cpu_baseline(workloads, m, k, n):
     t0 = time.perf_counter()
     while steps < 8 and (steps == 0 or time.perf_counter() - t0 < 10.0):
         A = oracle.quantize(c["x"], oracle.ROW16, oracle.FOUR_OVER_SIX)
-        oracle.gemm_f64(A, W)
+        C = oracle.gemm_f64(A, W)
         steps += 1
     dt = (time.perf_counter() - t0) / steps
-    return {"value": round(2 * m * n * k / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": steps,
-            "sample": f"{steps} full QKV steps: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and "
-                      "the fp64 GEMM against W [9216,3072] (W quantized once, untimed)"}
+    out = {"value": round(2 * m * n * k / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": steps,
+           "sample": f"{steps} full QKV steps: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and "
+                     "the fp64 GEMM against W [9216,3072] (W quantized once, untimed)"}
+    if gpu is None:
+        return out, None
+
+    def same(p, ref):
+        codes, scales, alpha = p
+        return bool(np.array_equal(codes, ref.codes) and np.array_equal(scales, ref.scales)
+                    and alpha.view(np.uint32) == np.float32(ref.alpha).view(np.uint32))
+
+    err = float(np.linalg.norm(gpu["y32"].astype(np.float64) - C) / np.linalg.norm(C))
+    parity = {"workload": "QKV input set 0 (seed 2), full size, against the CPU oracle",
+              "activation_codes_scales_alpha_bit_exact": same(gpu["a"], A),
+              "weight_codes_scales_alpha_bit_exact": same(gpu["w"], W),
+              "linear_fp32_rel_frobenius": err, "rel_frobenius_bound": 1e-5,
+              "linear_bf16_equals_rne_of_fp32": bool(np.array_equal(gpu["y16"], oracle.bf16_rne(gpu["y32"])))}
+    parity["pass"] = (parity["activation_codes_scales_alpha_bit_exact"] and
+                      parity["weight_codes_scales_alpha_bit_exact"] and err <= 1e-5 and
+                      parity["linear_bf16_equals_rne_of_fp32"])
+    return out, parity
 
 
 def main():
@@ -487,7 +538,7 @@ def main():
         "data": "synthetic (seeded normals shaped like a 5B video DiT's QKV projection)",
         "config": {"workload": "qkv_projection_x2640x3072_w9216x3072_bf16out",
                    "m": m, "k": k, "n": n, "rule": "four-over-six", "weight_blocks": "16x16",
-                   "act_blocks": "1x16"},
+                   "act_blocks": "1x16", "input_sets": 3, "seeds": [2, 102, 202]},
     }
     if "qkv" in parts:
         log("[bench] preparing QKV projection inputs")
@@ -525,8 +576,9 @@ def main():
         result["extra"] = bench_extra(nv, workloads, 20)
         torch.cuda.empty_cache()
     if "cpu" in parts:
-        log("[bench] CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(workloads, m, k, n)
+        log("[bench] CPU oracle baseline (and full-size parity of the first QKV set)")
+        gpu = gpu_outputs_for_parity(nv, workloads)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(workloads, m, k, n, gpu)
     print(json.dumps(result), flush=True)
 
 
