@@ -48,6 +48,7 @@ METRIC = "NVFP4 W4A4 GEMM TFLOPS incl. act-quantize at DiT shapes; KV-quantize G
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0       # dense fp16/bf16 MFMA, MI355X
 FP4_MFMA_PEAK_TFLOPS = 10100.0       # context only
+PEAK_SCLK_MHZ = 2400.0               # the shader clock the published peaks assume
 
 
 # HBM bytes per launch of the QKV-shaped GEMM kernel, from rocprofv3 byte
@@ -168,6 +169,19 @@ def read_gpu_clocks():
         if info:
             out[os.path.basename(os.path.dirname(dev))] = info
     return out or None
+
+
+def sclk_mhz(state):
+    """The shader clock in MHz from gpu_state's sysfs reading ("1: 2023Mhz *"),
+    or None."""
+    try:
+        for card in (state or {}).get("clocks", {}).values():
+            v = card.get("pp_dpm_sclk")
+            if v:
+                return float(v.split(":")[1].strip().lower().split("mhz")[0])
+    except (AttributeError, IndexError, ValueError):
+        return None
+    return None
 
 
 def gpu_state_under_load(step, seconds=2.0):
@@ -565,6 +579,14 @@ def main():
             "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gemm_traffic(),
             "kernel": "k_gemm_nvfp4", "kernel_ms": round(gms, 5), "algorithmic_flops_per_launch": flops,
             "frac_of_fp4_mfma_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4)}
+        # context: the same peak scaled to the shader clock read under load
+        # (the published peak assumes 2.4 GHz)
+        mhz = sclk_mhz(result.get("gpu_state"))
+        if mhz:
+            peak_clk = FP16_MFMA_PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ
+            result["roofline"]["sclk_mhz_under_load"] = mhz
+            result["roofline"]["peak_at_that_sclk"] = round(peak_clk, 1)
+            result["roofline"]["frac_at_that_sclk"] = round(achieved / peak_clk, 4)
         del sets
         torch.cuda.empty_cache()
     if "kv" in parts:

@@ -13,3 +13,11 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_sclk_parse():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.sclk_mhz({"clocks": {"card0": {"pp_dpm_sclk": "1: 2007Mhz *"}}}) == 2007.0
+    assert bench.sclk_mhz({"clocks": None}) is None
+    assert bench.sclk_mhz(None) is None
