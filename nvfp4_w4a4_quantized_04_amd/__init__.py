@@ -148,6 +148,25 @@ def _need_gpu(*ts):
                              "(call torch.cuda.set_device first)")
 
 
+def _check_out(out: torch.Tensor, shape, what="out"):
+    """A caller-supplied 2D output: exactly the shape the call writes, unit
+    column stride and rows that do not overlap (a padded row stride is passed
+    on to the library), float32 or bfloat16."""
+    if out.dim() != 2 or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(out.shape)}, the call writes {tuple(shape)}")
+    if shape[0] > 0 and shape[1] > 0 and (out.stride(1) != 1 or (shape[0] > 1 and out.stride(0) < shape[1])):
+        raise ValueError(f"{what} needs unit column stride and non-overlapping rows")
+    _out_dtype_code(out.dtype)
+
+
+def _check_vec(t, n, dtype, what):
+    """A contiguous 1D buffer the library reads or writes n elements of."""
+    if t is None:
+        return
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of at least {n} elements")
+
+
 @dataclass
 class NVFP4Tensor:
     """Packed NVFP4 tensor of logical shape [rows, cols].
@@ -177,6 +196,19 @@ def packed_shapes(rows: int, cols: int, block: int):
     return (cols, rows // 2), (cols, rows // 16)
 
 
+def _check_packed(t: NVFP4Tensor, rows: int, cols: int, block: int, what="packed tensor"):
+    """A packed tensor whose buffers the library reads or writes whole: uint8
+    codes and scales of exactly the layout's sizes, contiguous, and a float32
+    alpha."""
+    if t.block != block or t.rows != rows or t.cols != cols:
+        raise ValueError(f"{what}: block {t.block} [{t.rows}, {t.cols}], expected block {block} [{rows}, {cols}]")
+    cs, ss = packed_shapes(rows, cols, block)
+    for buf, shape, name in ((t.codes, cs, "codes"), (t.scales, ss, "scales")):
+        if buf.dtype != torch.uint8 or not buf.is_contiguous() or buf.numel() != shape[0] * shape[1]:
+            raise ValueError(f"{what}: {name} must be contiguous uint8 with {shape[0] * shape[1]} bytes")
+    _check_vec(t.alpha, 1, torch.float32, f"{what}: alpha")
+
+
 def empty_packed(rows: int, cols: int, block: int, device="cuda") -> NVFP4Tensor:
     cs, ss = packed_shapes(rows, cols, block)
     return NVFP4Tensor(torch.empty(cs, dtype=torch.uint8, device=device),
@@ -200,8 +232,10 @@ def quantize(x: torch.Tensor, block="row16", rule="4over6", amax: torch.Tensor |
         raise ValueError("x must be 2D with unit column stride")
     b = _block(block)
     rows, cols = x.shape
+    _check_vec(amax, 1, torch.float32, "amax")
     if out is None:
         out = empty_packed(rows, cols, b, x.device)
+    _check_packed(out, rows, cols, b, "out")
     if workspace is None and amax is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
     wsz = 0 if workspace is None else workspace.numel()
@@ -215,8 +249,10 @@ def quantize(x: torch.Tensor, block="row16", rule="4over6", amax: torch.Tensor |
 def dequantize(t: NVFP4Tensor, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
     """Xhat = (q * s) * alpha in the tensor's original orientation (``fp4_dequantize``)."""
     _need_gpu(t.codes)
+    _check_packed(t, t.rows, t.cols, t.block, "t")
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    _check_out(out, (t.rows, t.cols))
     _need_gpu(t.scales, t.alpha, out)
     _check("nvfp4_dequantize", lib.nvfp4_dequantize(
         _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, t.block,
@@ -233,8 +269,12 @@ def gemm(a: NVFP4Tensor, b: NVFP4Tensor, out_dtype=torch.float32, out: torch.Ten
     if k != kb:
         raise ValueError(f"contraction mismatch {k} vs {kb}")
     _need_gpu(ca, cb)
+    _check_packed(a, a.rows, a.cols, a.block, "a")
+    _check_packed(b, b.rows, b.cols, b.block, "b")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=ca.device)
+    _check_out(out, (m, n))
+    _check_vec(amax_out, 1, torch.float32, "amax_out")
     _need_gpu(sa, aa, sb, ab, out, amax_out)
     _check("nvfp4_gemm", lib.nvfp4_gemm(
         _ptr(ca), _ptr(sa), _ptr(aa), la, _ptr(cb), _ptr(sb), _ptr(ab), lb, m, n, k,
@@ -251,8 +291,10 @@ def kv_quantize(kv: torch.Tensor, rule="4over6", out: NVFP4Tensor | None = None,
         raise ValueError("kv must be contiguous")
     d = kv.shape[-1]
     vectors = kv.numel() // d if d else 0
+    _check_vec(amax, 1, torch.float32, "amax")
     if out is None:
         out = empty_packed(vectors, d, ROW16, kv.device)
+    _check_packed(out, vectors, d, ROW16, "out")
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(vectors, d), dtype=torch.uint8, device=kv.device)
     _need_gpu(amax, out.codes, out.scales, out.alpha, workspace)
@@ -278,8 +320,11 @@ def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4ove
     m, k = x.shape
     if k != kw:
         raise ValueError(f"in_features mismatch {k} vs {kw}")
+    _check_packed(w, w.rows, w.cols, w.block, "w")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _check_out(out, (m, n))
+    _check_vec(amax_out, 1, torch.float32, "amax_out")
     if workspace is None:
         workspace = linear_workspace(m, k, x.device)
     _need_gpu(cw, sw, aw, out, amax_out, workspace)
@@ -304,8 +349,11 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4ove
     t2, k = x.shape
     if t != t2 or dy.dtype != x.dtype:
         raise ValueError("dy and x need the same token count and dtype")
+    if dy.dim() != 2 or x.dim() != 2 or dy.stride(1) != 1 or x.stride(1) != 1:
+        raise ValueError("dy and x must be 2D with unit column stride")
     if out is None:
         out = torch.empty((n, k), dtype=out_dtype, device=x.device)
+    _check_out(out, (n, k))
     if workspace is None:
         workspace = wgrad_workspace(t, n, k, x.device)
     _need_gpu(out, workspace)
@@ -321,8 +369,10 @@ def transpose_tile16(t: NVFP4Tensor, out: NVFP4Tensor | None = None) -> NVFP4Ten
     if t.block != TILE16:
         raise ValueError("transpose_tile16 needs a TILE16 tensor")
     _need_gpu(t.codes)
+    _check_packed(t, t.rows, t.cols, TILE16, "t")
     if out is None:
         out = empty_packed(t.cols, t.rows, TILE16, t.codes.device)
+    _check_packed(out, t.cols, t.rows, TILE16, "out")
     _need_gpu(t.scales, t.alpha, out.codes, out.scales, out.alpha)
     _check("nvfp4_transpose_tile16", lib.nvfp4_transpose_tile16(
         _ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), t.rows, t.cols, _ptr(out.codes), _ptr(out.scales),
@@ -346,8 +396,10 @@ def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.T
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2D with unit column stride")
     rows, cols = x.shape
+    _check_vec(amax, 1, torch.float32, "amax")
     if out is None:
         out = empty_packed(rows, cols, COL16, x.device)
+    _check_packed(out, rows, cols, COL16, "out")
     if workspace is None and amax is None:
         workspace = torch.empty(lib.nvfp4_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=x.device)
     _need_gpu(out.codes, out.scales, out.alpha, workspace)
@@ -369,8 +421,10 @@ def kv_quantize_smoothed(k: torch.Tensor, rule="4over6", out: NVFP4Tensor | None
     v = k.numel() // d
     if out is None:
         out = empty_packed(v, d, ROW16, k.device)
+    _check_packed(out, v, d, ROW16, "out")
     if means is None:
         means = torch.empty(v, dtype=torch.float32, device=k.device)
+    _check_vec(means, v, torch.float32, "means")
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_kv_smooth_workspace_size(v, d), dtype=torch.uint8, device=k.device)
     _need_gpu(out.codes, out.scales, out.alpha, means, workspace)
@@ -395,12 +449,15 @@ def kv_dequantize_window(parts, out_dtype=torch.bfloat16, out: torch.Tensor | No
     for i, (t, means, first, count) in enumerate(parts):
         if t.block != ROW16 or t.cols != d:
             raise ValueError("segments must be ROW16 chunks of one head_dim")
+        _check_packed(t, t.rows, d, ROW16, f"segment {i}")
+        _check_vec(means, t.rows, torch.float32, f"segment {i} means")
         if first < 0 or count < 0 or first + count > t.rows:
             raise ValueError("segment rows out of range")
         _need_gpu(t.codes, t.scales, t.alpha, means)
         segs[i] = KvSegment(_ptr(t.codes), _ptr(t.scales), _ptr(t.alpha), _ptr(means), int(first), int(count))
     if out is None:
         out = torch.empty((rows, d), dtype=out_dtype, device=parts[0][0].codes.device)
+    _check_out(out, (rows, d))
     _need_gpu(out)
     _check("nvfp4_kv_dequantize_window", lib.nvfp4_kv_dequantize_window(
         segs, len(parts), d, _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _stream()))
@@ -451,10 +508,15 @@ def linear_lora(x: torch.Tensor, w: NVFP4Tensor, lora_a: torch.Tensor, lora_b: t
     r = lora_a.shape[0]
     if k != kw or lora_a.shape[1] != k or tuple(lora_b.shape) != (n, r):
         raise ValueError("shape mismatch")
+    _check_packed(w, w.rows, w.cols, w.block, "w")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _check_out(out, (m, n))
     if u is None:
         u = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
+    if tuple(u.shape) != (m, r) or u.dtype != torch.bfloat16 or not u.is_contiguous():
+        raise ValueError(f"u must be a contiguous bfloat16 [{m}, {r}] tensor")
+    _check_vec(amax_out, 1, torch.float32, "amax_out")
     if workspace is None:
         workspace = torch.empty(lib.nvfp4_linear_lora_workspace_size(m, k, r), dtype=torch.uint8, device=x.device)
     _need_gpu(cw, sw, aw, u, out, amax_out, workspace)
