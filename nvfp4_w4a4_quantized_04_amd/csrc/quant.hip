@@ -23,17 +23,21 @@ namespace nvfp4 {
 // block (kQuantThreads) must call both; all get the same alpha.
 static_assert(kMaxAmaxPartials <= kQuantThreads, "one partial per thread");
 
+// The load is unconditional (n_amax >= 1): a thread past the partials re-reads
+// the last one, which cannot change the max; with one amax every thread
+// reads it.
 __device__ __forceinline__ float alpha_issue(const float *__restrict__ amax_src, int n_amax)
 {
-    return n_amax > 1 && (int)threadIdx.x < n_amax ? amax_src[threadIdx.x] : 0.0f;
+    return amax_src[(int)threadIdx.x < n_amax ? (int)threadIdx.x : n_amax - 1];
 }
 
 __device__ __forceinline__ float alpha_finish(float part, const float *__restrict__ amax_src, int n_amax)
 {
+    (void)amax_src;
     __shared__ float red[kQuantThreads / 64];
     float a;
     if (n_amax == 1) {
-        a = amax_src[0];
+        a = part;
     } else {
         a = wave_max(part);
         if ((threadIdx.x & 63) == 0)
@@ -115,6 +119,38 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, 
     }
 }
 
+// The 16 values of one block from its raw 16-byte vectors (2 for bf16, 4 for fp32).
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4 (&raw)[sizeof(T)], float (&v)[16])
+{
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[2 * i] = bf16_lo(w[i]);
+            v[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            v[4 * q] = __uint_as_float(raw[q].x);
+            v[4 * q + 1] = __uint_as_float(raw[q].y);
+            v[4 * q + 2] = __uint_as_float(raw[q].z);
+            v[4 * q + 3] = __uint_as_float(raw[q].w);
+        }
+    }
+}
+
+// An empty tensor: only alpha (from the given amax or partials; 1 when 0).
+__global__ __launch_bounds__(kQuantThreads) void k_alpha_only(const float *__restrict__ amax_src, int n_amax,
+                                                              float *__restrict__ alpha_out)
+{
+    const float apart = alpha_issue(amax_src, n_amax);
+    const float alpha = alpha_finish(apart, amax_src, n_amax);
+    if (threadIdx.x == 0)
+        *alpha_out = alpha;
+}
+
 // ------------------------------------------------------ ROW16 (1D, along cols)
 
 // Each lane quantizes kRowBlocks whole 16-element blocks held in its own
@@ -133,22 +169,27 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
     const bool flat = ldx == bpr * 16;
     const int64_t b0 = (int64_t)blockIdx.x * (kQuantThreads * kRowBlocks) + threadIdx.x;
     // partial load, then the data loads; alpha and the kappa table are set up
-    // while the data is in flight
+    // while the data is in flight.  The data loads are unconditional (a lane
+    // past the end re-reads the last block and stores nothing) and the raw
+    // words are only unpacked after the table is built: a load under a
+    // branch, or a use of its value, would be waited for right there.
+    constexpr int kVec = (int)sizeof(T);                  // 16-byte vectors per block
     const float apart = alpha_issue(amax_src, n_amax);
-    float v[kRowBlocks][16];
+    uint4 raw[kRowBlocks][kVec];
 #pragma unroll
     for (int j = 0; j < kRowBlocks; j++) {
-        const int64_t b = b0 + j * kQuantThreads;
-        if (b < nb) {
-            int64_t off;
-            if (flat) {
-                off = b * 16;
-            } else {
-                const int64_t r = b / bpr;
-                off = r * ldx + (b - r * bpr) * 16;
-            }
-            load16(x + off, v[j]);
+        const int64_t b = b0 + j * kQuantThreads < nb ? b0 + j * kQuantThreads : nb - 1;   // nb >= 1
+        int64_t off;
+        if (flat) {
+            off = b * 16;
+        } else {
+            const int64_t r = b / bpr;
+            off = r * ldx + (b - r * bpr) * 16;
         }
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
+#pragma unroll
+        for (int u = 0; u < kVec; u++)
+            raw[j][u] = src[u];
     }
     const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
@@ -158,8 +199,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
     for (int j = 0; j < kRowBlocks; j++) {
         const int64_t b = b0 + j * kQuantThreads;
         if (b < nb) {
+            float v[16];
+            unpack16<T>(raw[j], v);
             uint32_t c0, c1, sb;
-            quant_block16<RULE4>(v[j], alpha, ktab, c0, c1, sb);
+            quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
             *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
             scales[b] = (uint8_t)sb;
         }
@@ -707,8 +750,7 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
 {
     if (rows == 0 || cols == 0) {
         // nothing to encode; alpha still follows the rule (amax 0 -> 1)
-        k_quant_row16<float, false><<<1, kQuantThreads, 0, s>>>(nullptr, 0, 0, 0, amax_src, n_amax, codes, scales,
-                                                                alpha);
+        k_alpha_only<<<1, kQuantThreads, 0, s>>>(amax_src, n_amax, alpha);
         return hipGetLastError();
     }
     if (dtype == 1) {
