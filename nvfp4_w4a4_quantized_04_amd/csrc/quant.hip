@@ -673,11 +673,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *
     const int cb = (int)(local - r * bpr);
     const int64_t v = sg.first + r;
     const int64_t blk = v * bpr + cb;
+    // the key mean is loaded with the codes and the scale (a segment without
+    // means reads alpha instead and ignores it): loaded under the branch, it
+    // would only be issued once the decode had waited for the others
+    const float *mp = sg.means ? sg.means + v : sg.alpha;
     const uint2 c = *reinterpret_cast<const uint2 *>(sg.codes + blk * 8);
+    const uint32_t sb = sg.scales[blk];
+    const float m = *mp;
+    __builtin_amdgcn_sched_barrier(0);         // all three loads issued before the decode
     float val[16];
-    decode16(c.x, c.y, e4m3_get<0>(sg.scales[blk]), *sg.alpha, val);
+    decode16(c.x, c.y, e4m3_get<0>(sb), *sg.alpha, val);
     if (sg.means) {
-        const float m = sg.means[v];
 #pragma unroll
         for (int i = 0; i < 16; i++)
             val[i] = val[i] + m;
