@@ -214,7 +214,9 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
  * architecture walkthrough page.
  */
 /* Workspace of nvfp4_linear_lora: nvfp4_linear's plus the partial sums of
- * the down projection (at most 8 * m * rank floats). */
+ * the down projection (at most 8 * m * rank floats) and up to 1024 partial
+ * maxima of |x| (the down projection reads all of x and leaves them for the
+ * activation quantizer, which then needs no amax pass of its own). */
 size_t nvfp4_linear_lora_workspace_size(int64_t m, int64_t k, int rank);
 
 nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,

@@ -242,7 +242,8 @@ size_t nvfp4_linear_lora_workspace_size(int64_t m, int64_t k, int rank)
 {
     if (m < 0 || k < 0 || rank < 0)
         return 0;
-    return nvfp4_linear_workspace_size(m, k) + round_up((size_t)kLoraMaxSlicesAbi * m * rank * 4, kAlignWs);
+    return nvfp4_linear_workspace_size(m, k) + round_up((size_t)kLoraMaxSlicesAbi * m * rank * 4, kAlignWs) +
+           round_up((size_t)kMaxAmaxSrc * 4, kAlignWs);
 }
 
 nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ldx, int rule,
@@ -281,13 +282,31 @@ nvfp4_status_t nvfp4_linear_lora(const void *x, int64_t m, int64_t k, int64_t ld
     uint8_t *codes = ws + kAlignWs + round_up(kAmaxBytes, kAlignWs);
     uint8_t *scales = codes + round_up((size_t)(m * k / 2), kAlignWs);
     float *lora_part = (float *)(ws + nvfp4_linear_workspace_size(m, k));
-    nvfp4_status_t st = do_quantize(x, NVFP4_BF16, m, k, ldx, NVFP4_ROW16, rule, nullptr, codes, scales, alpha,
-                                    partials, stream);
-    if (st != NVFP4_OK)
-        return st;
-    // U = x A^T (an empty contraction gives zeros)
-    st = launch_status(launch_lora_down((const uint16_t *)x, ldx, m, k, (const uint16_t *)lora_a, rank,
-                                        (uint16_t *)lora_u, lora_part, stream));
+    float *lora_amax = (float *)((uint8_t *)lora_part + round_up((size_t)kLoraMaxSlicesAbi * m * rank * 4, kAlignWs));
+    nvfp4_status_t st;
+    const int na = lora_amax_partials(m, k);
+    if (na >= 1 && na <= kMaxAmaxSrc) {
+        // U = x A^T in K-slice partials first: that kernel reads all of x and
+        // also leaves one max |x| per workgroup, which stand in for the
+        // quantizer's own amax pass; then the quantizer, then the sum into U
+        st = launch_status(launch_lora_partial((const uint16_t *)x, ldx, m, k, (const uint16_t *)lora_a, rank,
+                                               lora_part, lora_amax, stream));
+        if (st != NVFP4_OK)
+            return st;
+        st = launch_status(launch_quantize(x, NVFP4_BF16, m, k, ldx, NVFP4_ROW16, rule, lora_amax, na, codes, scales,
+                                           alpha, stream));
+        if (st != NVFP4_OK)
+            return st;
+        st = launch_status(launch_lora_reduce(m, k, rank, lora_part, (uint16_t *)lora_u, stream));
+    } else {
+        st = do_quantize(x, NVFP4_BF16, m, k, ldx, NVFP4_ROW16, rule, nullptr, codes, scales, alpha, partials,
+                         stream);
+        if (st != NVFP4_OK)
+            return st;
+        // U = x A^T (an empty contraction gives zeros)
+        st = launch_status(launch_lora_down((const uint16_t *)x, ldx, m, k, (const uint16_t *)lora_a, rank,
+                                            (uint16_t *)lora_u, lora_part, stream));
+    }
     if (st != NVFP4_OK)
         return st;
     GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};

@@ -14,6 +14,7 @@ constexpr int kAmaxThreads = 1024;      // threads per amax workgroup
 constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per amax thread
 constexpr int kMaxAmaxPartials = 256;   // amax pass: at most this many workgroups
 constexpr size_t kAmaxBytes = kMaxAmaxPartials * sizeof(float);
+constexpr int kMaxAmaxSrc = 1024;       // ROW16 quantize: at most this many amax partials (others: 256)
 
 // number of amax workgroups (= partial maxima) for a rows x cols tensor
 int amax_partials(int64_t rows, int64_t cols);
@@ -93,5 +94,12 @@ int lora_slices(int64_t m, int64_t k);
 constexpr int kLoraMaxSlicesAbi = 8;
 hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
                             uint16_t *u, float *partials, hipStream_t s);
+// The same in two launches: the K-slice partial products, which also write
+// one max |x| per workgroup to amax_part (lora_amax_partials(m, k) of them;
+// none when k == 0), then their sum into U.
+int lora_amax_partials(int64_t m, int64_t k);
+hipError_t launch_lora_partial(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
+                               float *partials, float *amax_part, hipStream_t s);
+hipError_t launch_lora_reduce(int64_t m, int64_t k, int r, const float *partials, uint16_t *u, hipStream_t s);
 
 }  // namespace nvfp4

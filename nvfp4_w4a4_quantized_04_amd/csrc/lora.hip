@@ -20,10 +20,15 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 constexpr int kLoraRowB = 64 * 2 + 16;   // LDS bytes per staged row (64 k + pad)
 
 
+// amax_part (optional): max |x| over the x chunks this workgroup staged
+// (rows m0..m0+31 of its K slice; clamped rows repeat row M-1), one float
+// per workgroup at blockIdx.y * gridDim.x + blockIdx.x.
 __global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict__ x, int64_t ldx, int M, int K,
                                                       const uint16_t *__restrict__ a, int r, int kslice,
-                                                      float *__restrict__ part)
+                                                      float *__restrict__ part, float *__restrict__ amax_part)
 {
+    __shared__ float red[4];
+    float xmax = 0.0f;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(32 + 128) * kLoraRowB];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5;
@@ -59,6 +64,13 @@ __global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict
             uint4 w = v[u];
             if (!((ok >> u) & 1))
                 w = make_uint4(0, 0, 0, 0);
+            if (q < 32 * 8) {                      // a chunk of x (rows 0-31)
+                const uint32_t e[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    xmax = fmaxf(xmax, fmaxf(fabsf(__uint_as_float(e[j] << 16)),
+                                             fabsf(__uint_as_float(e[j] & 0xffff0000u))));
+            }
             // past the end: the last chunk again (same value, same place)
             *reinterpret_cast<uint4 *>(buf + (q >> 3) * kLoraRowB + (q & 7) * 16) = w;
         }
@@ -88,6 +100,14 @@ __global__ __launch_bounds__(256) void k_lora_partial(const uint16_t *__restrict
             stash(lds[buf ^ 1], v, ok);
         __syncthreads();
         buf ^= 1;
+    }
+    if (amax_part) {
+        xmax = wave_max(xmax);
+        if (lane == 0)
+            red[wave] = xmax;
+        __syncthreads();
+        if (tid == 0)
+            amax_part[blockIdx.y * gridDim.x + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     }
     // lane l, register q: row m0 + l%32, column 32*wave + 8*(q/4) + 4*(l/32) + q%4
     if (active) {
@@ -124,25 +144,41 @@ int lora_slices(int64_t m, int64_t k)
     return (int)(sl < 1 ? 1 : sl);
 }
 
-hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
-                            uint16_t *u, float *partials, hipStream_t s)
+int lora_amax_partials(int64_t m, int64_t k)
 {
-    if (m == 0)
+    return k > 0 && m > 0 ? (int)((m + 31) / 32) * lora_slices(m, k) : 0;
+}
+
+hipError_t launch_lora_partial(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
+                               float *partials, float *amax_part, hipStream_t s)
+{
+    if (m == 0 || k == 0)
         return hipSuccess;
     const int sl = lora_slices(m, k);
     const int64_t steps = (k + 63) / 64;
     const int kslice = (int)((steps + sl - 1) / sl * 64);
-    if (k > 0) {
-        dim3 grid((unsigned)((m + 31) / 32), (unsigned)sl);
-        k_lora_partial<<<grid, 256, 0, s>>>(x, ldx, (int)m, (int)k, a, r, kslice, partials);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
+    dim3 grid((unsigned)((m + 31) / 32), (unsigned)sl);
+    k_lora_partial<<<grid, 256, 0, s>>>(x, ldx, (int)m, (int)k, a, r, kslice, partials, amax_part);
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_reduce(int64_t m, int64_t k, int r, const float *partials, uint16_t *u, hipStream_t s)
+{
+    if (m == 0)
+        return hipSuccess;
     const int64_t n = m * r;
     // k == 0: no partial was written and U is zero
-    k_lora_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, k > 0 ? sl : 0, n, u);
+    k_lora_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partials, k > 0 ? lora_slices(m, k) : 0, n, u);
     return hipGetLastError();
+}
+
+hipError_t launch_lora_down(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, const uint16_t *a, int r,
+                            uint16_t *u, float *partials, hipStream_t s)
+{
+    const hipError_t e = launch_lora_partial(x, ldx, m, k, a, r, partials, nullptr, s);
+    if (e != hipSuccess)
+        return e;
+    return launch_lora_reduce(m, k, r, partials, u, s);
 }
 
 }  // namespace nvfp4

@@ -23,12 +23,19 @@ namespace nvfp4 {
 // block (kQuantThreads) must call both; all get the same alpha.
 static_assert(kMaxAmaxPartials <= kQuantThreads, "one partial per thread");
 
-// The load is unconditional (n_amax >= 1): a thread past the partials re-reads
-// the last one, which cannot change the max; with one amax every thread
-// reads it.
+// The loads are unconditional (n_amax >= 1): a thread past the partials
+// re-reads the last one, which cannot change the max; with one amax every
+// thread reads it.  NPT: partials per thread (up to NPT * kQuantThreads).
+template <int NPT = 1>
 __device__ __forceinline__ float alpha_issue(const float *__restrict__ amax_src, int n_amax)
 {
-    return amax_src[(int)threadIdx.x < n_amax ? (int)threadIdx.x : n_amax - 1];
+    float a = amax_src[(int)threadIdx.x < n_amax ? (int)threadIdx.x : n_amax - 1];
+#pragma unroll
+    for (int j = 1; j < NPT; j++) {
+        const int i = (int)threadIdx.x + j * kQuantThreads;
+        a = fmaxf(a, amax_src[i < n_amax ? i : n_amax - 1]);
+    }
+    return a;
 }
 
 __device__ __forceinline__ float alpha_finish(float part, const float *__restrict__ amax_src, int n_amax)
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_alpha_only(const float *__res
 // registers (blocks b, b+256, ... of the workgroup's range, so every load and
 // store instruction of a wave is contiguous).  Blocks are numbered row-major:
 // block b's codes are bytes [8b, 8b+8), its scale is byte b (cols % 16 == 0).
-template <typename T, bool RULE4>
+template <typename T, bool RULE4, int NPT = 1>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restrict__ x, int64_t rows, int64_t bpr,
                                                                int64_t ldx, const float *__restrict__ amax_src,
                                                                int n_amax, uint8_t *__restrict__ codes,
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
     // words are only unpacked after the table is built: a load under a
     // branch, or a use of its value, would be waited for right there.
     constexpr int kVec = (int)sizeof(T);                  // 16-byte vectors per block
-    const float apart = alpha_issue(amax_src, n_amax);
+    const float apart = alpha_issue<NPT>(amax_src, n_amax);
     uint4 raw[kRowBlocks][kVec];
 #pragma unroll
     for (int j = 0; j < kRowBlocks; j++) {
@@ -724,7 +731,12 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
         const int64_t nb = rows * bpr;
         const int64_t per_wg = (int64_t)kQuantThreads * kRowBlocks;
         const unsigned grid = (unsigned)((nb + per_wg - 1) / per_wg);
-        k_quant_row16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
+        if (n_amax > kQuantThreads)             // up to kMaxAmaxSrc partials (four per thread)
+            k_quant_row16<T, R4, kMaxAmaxSrc / kQuantThreads><<<grid, kQuantThreads, 0, s>>>(
+                x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
+        else
+            k_quant_row16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales,
+                                                                alpha);
     } else if (block == 1) {
         const int64_t tpr = cols / 16;
         const int64_t ty = rows / 16 < 65535 ? rows / 16 : 65535;
