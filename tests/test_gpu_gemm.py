@@ -203,3 +203,29 @@ def test_linear_lora(m, n, k, r):
     ref = oracle.linear_lora_f64(A, W, ug, lb, scale)
     assert rel_frobenius(host_bits(y), ref) <= GEMM_RTOL
     assert np.array_equal(host_bits(y16), oracle.bf16_rne(host_bits(y)))
+
+
+@pytest.mark.parametrize("m", [32768, 32800])
+def test_linear_lora_amax_from_down_projection_limit(m):
+    """The LoRA linear takes the activation amax from the down projection's
+    per-workgroup maxima while there are at most 1024 of them (m = 32768,
+    k = 64: 1024 row blocks of one K slice) and runs its own amax pass past
+    that (m = 32800: 1025): both give the oracle's codes, hence its result."""
+    k, n, r = 64, 64, 32
+    print(f"[case] linear_lora amax partials m={m}", flush=True)
+    rng = np.random.default_rng(m)
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    x[m // 2 + 7, 5] = workloads.f32_to_bf16_bits(np.array([50.0], np.float32))[0]   # the max in a late block
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    la = workloads.f32_to_bf16_bits((rng.standard_normal((r, k)) / 8).astype(np.float32))
+    lb = workloads.f32_to_bf16_bits((rng.standard_normal((n, r)) * 0.02).astype(np.float32))
+    W = oracle.quantize(w, oracle.TILE16, 1)
+    y, u = nv.linear_lora(dev_from_host(x), packed_to_device(W), dev_from_host(la), dev_from_host(lb), 1.0,
+                          torch.float32)
+    torch.cuda.synchronize()
+    ug = host_bits(u)
+    check_lora_u(ug, x, la)
+    A = oracle.quantize(x, oracle.ROW16, 1)
+    ref = oracle.linear_lora_f64(A, W, ug, lb, 1.0)
+    assert rel_frobenius(host_bits(y), ref) <= GEMM_RTOL
+
