@@ -206,7 +206,11 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
  * the adapter scale (alpha / rank).  lora_u: caller buffer [m][rank] bf16
  * that receives U (x A^T with fp32 accumulation, rounded once to bf16, as a
  * bf16 linear layer computes it).  The rank-r update runs on bf16 MFMA in the
- * same GEMM launch after the NVFP4 contraction; fp32 accumulation.  Other
+ * same GEMM launch after the NVFP4 contraction; fp32 accumulation.  Both bf16
+ * products run on the matrix cores, which flush fp32 subnormal products and
+ * partial sums (below 2^-126) to zero: rows of x that are themselves near
+ * the bottom of the bf16 range get U within k * 2^-126 of the exact sum,
+ * not its rounding.  Other
  * arguments as nvfp4_linear; workspace >= nvfp4_linear_lora_workspace_size().
  * Source: "LoRA parameterization" (W ~ Dequant(Q(W0)) + (alpha/r) B A, rank
  * 128, alpha 128, BF16 adapters) and the NVFP4 Inference section (the

@@ -57,14 +57,19 @@ def packed_to_device(p: oracle.Packed):
 def check_lora_u(ug: np.ndarray, x: np.ndarray, la: np.ndarray):
     """U from the kernel is a correct bf16 rounding of a sum within the fp32
     accumulation bound of x A^T: |U - exact| <= half a bf16 step of U plus
-    K * 2^-24 * sum |x a|; and it equals the oracle's rounding of the exact
-    sum except where the two sums straddle a rounding point (rare)."""
+    K * 2^-24 * sum |x a|, plus K * 2^-126 because the matrix cores flush fp32
+    subnormal products and partial sums (below 2^-126) to zero; and, where the
+    exact sum is far above that range, it equals the oracle's rounding of the
+    exact sum except where the two sums straddle a rounding point (rare)."""
     xf = workloads.bf16_to_f32(x).astype(np.float64)
     af = workloads.bf16_to_f32(la).astype(np.float64)
     exact = xf @ af.T
-    bound = xf.shape[1] * 2.0 ** -24 * (np.abs(xf) @ np.abs(af).T)
+    k = xf.shape[1]
+    bound = k * 2.0 ** -24 * (np.abs(xf) @ np.abs(af).T)
     u = workloads.bf16_to_f32(ug).astype(np.float64)
     step = np.abs(u) * 2.0 ** -7                       # one bf16 step at |u| (or more)
-    assert np.all(np.abs(u - exact) <= 0.5 * step + bound + 1e-300)
+    assert np.all(np.abs(u - exact) <= 0.5 * step + bound + k * 2.0 ** -126)
     uref = oracle.lora_down_bf16(x, la)
-    assert np.mean(ug == uref) >= 0.99
+    normal = np.abs(exact) >= 2.0 ** -100
+    if np.any(normal):
+        assert np.mean(ug[normal] == uref[normal]) >= 0.99

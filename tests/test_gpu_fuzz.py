@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, dev_from_host, host_bits, packed_to_device,
-                               rel_frobenius)
+from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, check_lora_u, dev_from_host, host_bits,
+                               packed_to_device, rel_frobenius)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,49 @@ def test_fuzz_col16(seed):
     got = nv.quantize(dev_from_host(x), "col16", rule)
     torch.cuda.synchronize()
     assert_packed_equal(got, ref, f"col16 {rows}x{cols}")
+
+
+def _lora_cases(n=10, seed=77):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        m = int(g.integers(1, 700))
+        k = 16 * int(g.integers(1, 60))
+        nn = int(g.integers(1, 400))
+        r = 32 * int(g.integers(1, 5))
+        out.append((i, m, nn, k, r, MIXES[i % len(MIXES)], int(g.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _lora_cases(), ids=lambda c: f"l{c[0]}_m{c[1]}_n{c[2]}_k{c[3]}_r{c[4]}_{c[5]}")
+def test_fuzz_linear_lora(case):
+    """The W4A4 + LoRA linear (bf16 x): U = bf16(x A^T) within the fp32
+    accumulation bound, y against the fp64 reference built on the oracle's
+    activation codes and the kernel's U, bf16 y = RNE of the fp32 y."""
+    i, m, n, k, r, mix, rule = case
+    print(f"[case] fuzz lora {case}", flush=True)
+    g = np.random.default_rng(5000 + i)
+    x = workloads.f32_to_bf16_bits(_data(g, (m, k), mix))
+    w = workloads.f32_to_bf16_bits((g.standard_normal((n, k)) * 0.02).astype(np.float32))
+    la = workloads.f32_to_bf16_bits((g.standard_normal((r, k)) / np.sqrt(k)).astype(np.float32))
+    lb = workloads.f32_to_bf16_bits((g.standard_normal((n, r)) * 0.02).astype(np.float32))
+    W = oracle.quantize(w, oracle.TILE16 if n % 16 == 0 else oracle.ROW16, rule)
+    Wd = packed_to_device(W)
+    scale = float(g.uniform(0.25, 2.0))
+    y, u = nv.linear_lora(dev_from_host(x), Wd, dev_from_host(la), dev_from_host(lb), scale, torch.float32,
+                          rule=rule)
+    y16, u16 = nv.linear_lora(dev_from_host(x), Wd, dev_from_host(la), dev_from_host(lb), scale, torch.bfloat16,
+                              rule=rule)
+    torch.cuda.synchronize()
+    ug = host_bits(u)
+    assert np.array_equal(ug, host_bits(u16))
+    check_lora_u(ug, x, la)
+    A = oracle.quantize(x, oracle.ROW16, rule)
+    ref = oracle.linear_lora_f64(A, W, ug, lb, scale)
+    gy = host_bits(y)
+    if np.any(ref):
+        assert rel_frobenius(gy, ref) <= GEMM_RTOL
+    else:
+        assert not np.any(gy)
+    assert np.array_equal(host_bits(y16), oracle.bf16_rne(gy))
+
