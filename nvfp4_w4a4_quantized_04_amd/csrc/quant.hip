@@ -766,6 +766,9 @@ hipError_t launch_quantize(const void *x, int dtype, int64_t rows, int64_t cols,
                            const float *amax_src, int n_amax, uint8_t *codes, uint8_t *scales, float *alpha,
                            hipStream_t s, int rht_signs)
 {
+    // the kernels read at most kMaxAmaxSrc partials (ROW16) or kQuantThreads (the others)
+    if (n_amax < 1 || n_amax > (block == 0 ? kMaxAmaxSrc : kQuantThreads))
+        return hipErrorInvalidValue;
     if (rows == 0 || cols == 0) {
         // nothing to encode; alpha still follows the rule (amax 0 -> 1)
         k_alpha_only<<<1, kQuantThreads, 0, s>>>(amax_src, n_amax, alpha);
