@@ -612,18 +612,24 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_quant_smoothed(const T *__
     const int64_t nb = vectors << g_log2;
     const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
     const float apart = alpha_issue(amax_src, n_amax);
-    float f[16];
-    float mean = 0.0f;
-    if (b < nb) {
-        load16(x + b * 16, f);
-        mean = means[b >> g_log2];
-    }
+    // data and mean loads without a branch (a lane past the end re-reads the
+    // last block and stores nothing; nb >= 1), unpacked only after alpha and
+    // the kappa table, as in k_quant_row16
+    const int64_t bc = b < nb ? b : nb - 1;
+    uint4 raw[sizeof(T)];
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + bc * 16);
+#pragma unroll
+    for (int u = 0; u < (int)sizeof(T); u++)
+        raw[u] = src[u];
+    const float mean = means[bc >> g_log2];
     const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
     if (b >= nb)
         return;
+    float f[16];
+    unpack16<T>(raw, f);
 #pragma unroll
     for (int i = 0; i < 16; i++)
         f[i] = f[i] - mean;
@@ -842,7 +848,11 @@ hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, 
     if (e != hipSuccess)
         return e;
     const int64_t nb = vectors << g_log2;
-    const unsigned grid = (unsigned)(nb > 0 ? (nb + kQuantThreads - 1) / kQuantThreads : 1);
+    if (nb == 0) {
+        k_alpha_only<<<1, kQuantThreads, 0, s>>>(partials, n, alpha);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)((nb + kQuantThreads - 1) / kQuantThreads);
     if (dtype == 1) {
         if (rule) k_kv_quant_smoothed<uint16_t, true><<<grid, kQuantThreads, 0, s>>>((const uint16_t *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
         else      k_kv_quant_smoothed<uint16_t, false><<<grid, kQuantThreads, 0, s>>>((const uint16_t *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);

@@ -32,6 +32,22 @@ def test_kv_quantize_smoothed(vectors, d):
     assert np.array_equal(host_bits(means).view(np.uint32), ref_means.view(np.uint32))
 
 
+def test_kv_quantize_smoothed_empty_and_constant():
+    # no keys: only alpha is written, the oracle's 1.0 for a zero amax;
+    # constant keys smooth to exact zeros
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    got, means = nv.kv_quantize_smoothed(x)
+    torch.cuda.synchronize()
+    ref, _ = oracle.kv_quantize_smoothed(np.zeros((0, 128), np.uint16))
+    assert got.alpha.item() == ref.alpha and got.codes.numel() == 0 and means.numel() == 0
+    k = workloads.f32_to_bf16_bits(np.full((33, 64), 3.5, np.float32))
+    ref, ref_means = oracle.kv_quantize_smoothed(k)
+    got, means = nv.kv_quantize_smoothed(dev_from_host(k))
+    torch.cuda.synchronize()
+    assert_packed_equal(got, ref, "smoothed constant")
+    assert np.array_equal(host_bits(means).view(np.uint32), ref_means.view(np.uint32))
+
+
 def test_kv_quantize_smoothed_fp32_input():
     rng = np.random.default_rng(3)
     k = (rng.standard_normal((96, 128)) + 5).astype(np.float32)
