@@ -309,7 +309,8 @@ size_t nvfp4_kv_smooth_workspace_size(int64_t vectors, int64_t head_dim);
  * fp32 order: per 16-element block a partial sum in index order, the
  * partials added in block order, mean = sum / head_dim, key - mean.
  * k: [vectors][head_dim] contiguous, 16-byte aligned; workspace >=
- * nvfp4_kv_smooth_workspace_size().
+ * nvfp4_kv_smooth_workspace_size().  vectors == 0 writes only alpha (1.0,
+ * the zero-amax value).
  * Source: "Key smoothing" (subtract the mean over the head dimension from
  * each key vector) and "Chunkwise quantization procedure" (per-chunk,
  * per-layer global scale), NVFP4 Inference section of the architecture
