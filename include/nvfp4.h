@@ -63,8 +63,10 @@
  *     (nvfp4_gemm, nvfp4_linear, nvfp4_linear_lora, nvfp4_wgrad and the
  *     DGRAD use of nvfp4_linear) also need each packed operand below 4 GiB
  *     (rows * k / 2 < 2^32 for both A and B) and fewer than 2^23 output
- *     tiles of 128 x 128 (about 2^37 output elements); larger calls return
- *     NVFP4_ERR_SHAPE.
+ *     tiles of 128 x 128 (about 2^37 output elements).  The quantize,
+ *     dequantize, transpose and smoothed-key entry points launch one lane
+ *     per 16-element block and a dispatch counts lanes in 32 bits: at most
+ *     2^36 - 2^20 elements per call.  Larger calls return NVFP4_ERR_SHAPE.
  *   - Numeric contract: inputs finite and amax == 0 or amax >= 2^-96;
  *     otherwise results are unspecified, but no call faults.
  */

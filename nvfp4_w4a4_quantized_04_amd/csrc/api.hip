@@ -18,6 +18,10 @@ inline bool dtype_ok(int d) { return d == NVFP4_F32 || d == NVFP4_BF16; }
 inline bool rule_ok(int r) { return r == NVFP4_RULE_STATIC6 || r == NVFP4_RULE_4OVER6; }
 inline bool block_ok(int b) { return b == NVFP4_ROW16 || b == NVFP4_TILE16 || b == NVFP4_COL16; }
 inline bool dims_ok(int64_t r, int64_t c) { return r >= 0 && c >= 0 && r < kMaxDim && c < kMaxDim; }
+// The quantize, dequantize and transpose kernels launch up to one lane per
+// 16-element block, and a dispatch counts work-items in 32 bits: at most
+// 2^32 - 2^16 blocks, 2^36 - 2^20 elements (rows, cols < 2^31: no overflow).
+inline bool lanes_fit(int64_t r, int64_t c) { return r * c / 16 <= ((int64_t)1 << 32) - ((int64_t)1 << 16); }
 // The GEMM's producer waves address each packed operand ([rows][k/2] code
 // bytes) with 32-bit byte offsets: both operands must stay below 4 GiB.  Its
 // launch has 512 threads per output tile (at least 128 x 128) and a dispatch
@@ -44,7 +48,7 @@ nvfp4_status_t check_quant_args(const void *x, int x_dtype, int64_t rows, int64_
 {
     if (!dtype_ok(x_dtype) || !rule_ok(rule) || !block_ok(block))
         return NVFP4_ERR_DTYPE;
-    if (!dims_ok(rows, cols) || !block_shape_ok(block, rows, cols) || ldx < cols)
+    if (!dims_ok(rows, cols) || !lanes_fit(rows, cols) || !block_shape_ok(block, rows, cols) || ldx < cols)
         return NVFP4_ERR_SHAPE;
     if (!alpha)
         return NVFP4_ERR_NULL;
@@ -143,7 +147,7 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, con
 {
     if (!dtype_ok(y_dtype) || !block_ok(block))
         return NVFP4_ERR_DTYPE;
-    if (!dims_ok(rows, cols) || !block_shape_ok(block, rows, cols) || ldy < cols)
+    if (!dims_ok(rows, cols) || !lanes_fit(rows, cols) || !block_shape_ok(block, rows, cols) || ldy < cols)
         return NVFP4_ERR_SHAPE;
     if (rows > 0 && cols > 0 && (!codes || !scales || !alpha || !y))
         return NVFP4_ERR_NULL;
@@ -370,7 +374,7 @@ nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scale
                                      int64_t rows, int64_t cols, uint8_t *codes_t, uint8_t *scales_t,
                                      float *alpha_t, hipStream_t stream)
 {
-    if (!dims_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0)
+    if (!dims_ok(rows, cols) || !lanes_fit(rows, cols) || rows % 16 != 0 || cols % 16 != 0)
         return NVFP4_ERR_SHAPE;
     if (!alpha || !alpha_t)
         return NVFP4_ERR_NULL;
@@ -414,7 +418,8 @@ nvfp4_status_t nvfp4_kv_quantize_smoothed(const void *k, int k_dtype, int64_t ve
 {
     if (!dtype_ok(k_dtype) || !rule_ok(rule))
         return NVFP4_ERR_DTYPE;
-    if (!dims_ok(vectors, head_dim) || head_dim < 16 || head_dim > 1024 || (head_dim & (head_dim - 1)) != 0)
+    if (!dims_ok(vectors, head_dim) || !lanes_fit(vectors, head_dim) || head_dim < 16 || head_dim > 1024 ||
+        (head_dim & (head_dim - 1)) != 0)
         return NVFP4_ERR_SHAPE;
     if (!alpha || (vectors > 0 && (!k || !codes || !scales || !means)))
         return NVFP4_ERR_NULL;

@@ -115,6 +115,27 @@ def test_transpose_tile16_validation_without_gpu():
     assert t(FAKE, FAKE, FAKE, 32, 32, FAKE + 8, FAKE, FAKE, None) == 3    # codes_t alignment
 
 
+def test_dispatch_size_limit_without_gpu():
+    # one lane per 16-element block and 32-bit work-item counts: at most
+    # 2^32 - 2^16 blocks; each dimension alone stays below 2^31
+    import nvfp4_w4a4_quantized_04_amd as m
+    big_r, big_c = 1 << 22, 1 << 14                 # 2^36 elements: 2^32 blocks
+    ok_r = big_r - 64                               # 2^32 - 2^16 blocks, the largest accepted
+    q = m.lib.nvfp4_quantize
+    assert q(FAKE, 1, big_r, big_c, big_c, 0, 1, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 2
+    assert q(FAKE, 1, ok_r, big_c, big_c, 0, 1, FAKE, FAKE, FAKE, None, None, 0, None) == 1   # shape passes
+    assert q(FAKE, 1, big_r, big_c, big_c, 2, 1, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 2
+    d = m.lib.nvfp4_dequantize
+    assert d(FAKE, FAKE, FAKE, big_r, big_c, 0, FAKE, 1, big_c, None) == 2
+    assert d(FAKE, FAKE, FAKE, ok_r, big_c, 0, None, 1, big_c, None) == 1
+    t = m.lib.nvfp4_transpose_tile16
+    assert t(FAKE, FAKE, FAKE, big_r, big_c, FAKE, FAKE, FAKE, None) == 2
+    assert t(FAKE, FAKE, None, ok_r, big_c, FAKE, FAKE, FAKE, None) == 1
+    k = m.lib.nvfp4_kv_quantize_smoothed
+    assert k(FAKE, 1, 1 << 26, 1024, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2
+    assert k(FAKE, 1, (1 << 26) - 1024, 1024, 1, FAKE, FAKE, FAKE, None, FAKE, 4096, None) == 1
+
+
 def test_hip_build_script_loads_without_the_library():
     # the build must work on a tree where libnvfp4.so does not exist yet
     import __graft_entry__ as ge
