@@ -229,7 +229,7 @@ constexpr int kColCols = 128;                       // columns per workgroup
 constexpr int kColGroupRB = 16;                     // row-blocks per group (4 waves x 4 steps)
 constexpr int kColCodePitch = kColGroupRB * 8 + 16; // LDS bytes per column of parked codes
 
-template <typename T, bool RULE4, bool RHT>
+template <typename T, bool RULE4, bool RHT, bool PAIR>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                                int64_t ldx, const float *__restrict__ amax_src,
                                                                int n_amax, uint8_t *__restrict__ codes,
@@ -249,18 +249,23 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
     const int64_t col0 = (int64_t)blockIdx.x * kColCols;
     const int64_t c = col0 + 2 * lane;                  // this lane's first column
     const bool c0ok = c < cols, c1ok = c + 1 < cols;
-    // both columns in one 2-element vector load
-    const bool pair = c1ok && ldx % 2 == 0 && reinterpret_cast<uintptr_t>(x) % (2 * sizeof(T)) == 0;
+    // PAIR (chosen by the launcher: even column count, ldx and x aligned to a
+    // pair): both columns in one 2-element vector load, with no branch at all,
+    // so that the loads stay in flight across the alpha set-up
+    const int64_t cp = c0ok ? c : cols - 2;             // lanes past the last column re-read the last pair
 
-    // the 16 rows x 2 columns of row-block rb, as 16 packed pairs
+    // the 16 rows x 2 columns of row-block rb, as 16 packed pairs; a row-block
+    // past the end re-reads the last one (nrb >= 1; its results are not stored)
     typedef typename std::conditional<sizeof(T) == 2, uint32_t, uint2>::type Pair;
     auto load_block = [&](int64_t rb, Pair (&v)[16]) {
-        const T *p = x + rb * 16 * ldx + c;
-        if (pair) {
+        rb = rb < nrb ? rb : nrb - 1;
+        if constexpr (PAIR) {
+            const T *p = x + rb * 16 * ldx + cp;
 #pragma unroll
             for (int i = 0; i < 16; i++)
                 v[i] = *reinterpret_cast<const Pair *>(p + i * ldx);
         } else {
+            const T *p = x + rb * 16 * ldx + c;
 #pragma unroll
             for (int i = 0; i < 16; i++) {
                 T e[2] = {T(0), T(0)};
@@ -277,23 +282,28 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_col16(const T *__restri
     // kappa table are set up
     Pair v[2][16];
     const int64_t gfirst = (int64_t)blockIdx.y * kColGroupRB;
-    if (gfirst < nrb && gfirst + wave < nrb)
-        load_block(gfirst + wave, v[0]);
+    load_block(gfirst + wave, v[0]);                    // gfirst < nrb: grid.y <= the group count
     const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         *alpha_out = alpha;
 
-    for (int64_t g0 = gfirst; g0 < nrb; g0 += (int64_t)gridDim.y * kColGroupRB) {
+    static_assert(kSteps % 2 == 0, "the next group's first row-block goes to v[0]");
+    const int64_t gstride = (int64_t)gridDim.y * kColGroupRB;
+    for (int64_t g0 = gfirst; g0 < nrb; g0 += gstride) {
         const int ng = nrb - g0 < kColGroupRB ? (int)(nrb - g0) : kColGroupRB;
         int64_t rb = g0 + wave;
-        if (g0 != gfirst && wave < ng)
-            load_block(rb, v[0]);
 #pragma unroll
         for (int st = 0; st < kSteps; st++) {
             const int slot = st * kWaves + wave;            // row-block index inside the group
-            if (st + 1 < kSteps && slot + kWaves < ng)
+            // every step prefetches the next one; the last step prefetches the
+            // next group's first row-block, or re-reads its own (a cache hit)
+            if (st + 1 < kSteps) {
                 load_block(rb + kWaves, v[(st + 1) & 1]);
+            } else {
+                const int64_t nx = g0 + gstride + wave;
+                load_block(nx < nrb ? nx : rb, v[0]);
+            }
             if (slot < ng) {
 #pragma unroll
                 for (int k = 0; k < 2; k++) {
@@ -759,12 +769,15 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
         if (gy > 65535) gy = 65535;
         if (gy < 1) gy = 1;
         dim3 grid((unsigned)gx, (unsigned)gy);
+        const bool pair = cols % 2 == 0 && ldx % 2 == 0 && reinterpret_cast<uintptr_t>(x) % (2 * sizeof(T)) == 0;
+        const uint32_t signs = rht_signs >= 0 ? (uint32_t)rht_signs : 0u;
+        auto go = [&](auto kernel) {
+            kernel<<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes, scales, alpha, signs);
+        };
         if (rht_signs >= 0)
-            k_quant_col16<T, R4, true><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes,
-                                                                      scales, alpha, (uint32_t)rht_signs);
+            pair ? go(k_quant_col16<T, R4, true, true>) : go(k_quant_col16<T, R4, true, false>);
         else
-            k_quant_col16<T, R4, false><<<grid, kQuantThreads, 0, s>>>(x, rows, cols, ldx, amax_src, n_amax, codes,
-                                                                       scales, alpha, 0u);
+            pair ? go(k_quant_col16<T, R4, false, true>) : go(k_quant_col16<T, R4, false, false>);
     }
 }
 

@@ -66,6 +66,16 @@ def test_col16_many_row_tiles():
     _case(x, oracle.COL16, 1)
 
 
+@pytest.mark.parametrize("cols", [2, 34])
+def test_col16_paired_loads_across_groups(cols):
+    # even column count (paired loads), 1801 groups of 16 row-blocks on 901
+    # grid rows: workgroups take two groups, and the last group (5 row-blocks)
+    # is a workgroup's second one, so each group's prefetch of the next is used
+    rows = 16 * (16 * 1800 + 5)
+    x = workloads.random_bf16(13 + cols, (rows, cols), 1.0, 0.001)
+    _case(x, oracle.COL16, 1)
+
+
 @pytest.mark.parametrize("shape", [(16, 1), (64, 257), (2064, 130), (4144, 192), (2048, 3072)])
 @pytest.mark.parametrize("signs", [0x0000, 0xB6E3])
 def test_col16_rht_bf16_shapes(shape, signs):
