@@ -326,7 +326,7 @@ def _bf16_or_f32(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float32)
 
 
-def _bf16_rne_f64(y: np.ndarray) -> np.ndarray:
+def bf16_rne_f64(y: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (nearest, ties to even) in one step: the
     exact bf16 neighbours of each value are compared in fp64."""
     y = np.asarray(y, np.float64)
@@ -348,6 +348,9 @@ def _bf16_rne_f64(y: np.ndarray) -> np.ndarray:
         tie = (err[k] == e_best) & (((cand[k] >> 16) & 1) == 0) & (cand[k] != out)
         out = np.where(tie, cand[k], out)
     return (out >> 16).astype(np.uint16)
+
+
+_bf16_rne_f64 = bf16_rne_f64
 
 
 def transpose_tile16(p: Packed) -> Packed:

@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, check_lora_u, dev_from_host, host_bits,
-                               packed_to_device, rel_frobenius)
+from tests.gpu_helpers import (GEMM_RTOL, assert_packed_equal, check_lora_u, check_y_on_oracle_u, dev_from_host,
+                               host_bits, lora_branch_allowance, packed_to_device, rel_frobenius)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,9 +120,11 @@ def _lora_cases(n=10, seed=77):
 
 @pytest.mark.parametrize("case", _lora_cases(), ids=lambda c: f"l{c[0]}_m{c[1]}_n{c[2]}_k{c[3]}_r{c[4]}_{c[5]}")
 def test_fuzz_linear_lora(case):
-    """The W4A4 + LoRA linear (bf16 x): U = bf16(x A^T) within the fp32
-    accumulation bound, y against the fp64 reference built on the oracle's
-    activation codes and the kernel's U, bf16 y = RNE of the fp32 y."""
+    """The W4A4 + LoRA linear (bf16 x): U equal to the oracle's rounding of
+    the exact sums outside the fp32 rounding windows, y against the reference
+    built wholly by the oracle (allowing only the effect of U elements inside
+    such windows) and against the reference on the kernel's U, bf16 y = RNE
+    of the fp32 y."""
     i, m, n, k, r, mix, rule = case
     print(f"[case] fuzz lora {case}", flush=True)
     g = np.random.default_rng(5000 + i)
@@ -142,8 +144,10 @@ def test_fuzz_linear_lora(case):
     assert np.array_equal(ug, host_bits(u16))
     check_lora_u(ug, x, la)
     A = oracle.quantize(x, oracle.ROW16, rule)
-    ref = oracle.linear_lora_f64(A, W, ug, lb, scale)
     gy = host_bits(y)
+    uo = oracle.lora_down_bf16(x, la)
+    check_y_on_oracle_u(gy, oracle.linear_lora_f64(A, W, uo, lb, scale), lora_branch_allowance(ug, uo, lb, scale))
+    ref = oracle.linear_lora_f64(A, W, ug, lb, scale)
     if np.any(ref):
         assert rel_frobenius(gy, ref) <= GEMM_RTOL
     else:

@@ -266,24 +266,32 @@ def _near_tie(xs, alpha, m):
     return False
 
 
-def _compare_exact(x, rule=FOUR_OVER_SIX):
-    p = oracle.quantize(x, ROW16, rule)
+def _compare_exact(x, rule=FOUR_OVER_SIX, block=ROW16):
+    """Every block of x (ROW16: 16 along a row; TILE16: a 16x16 tile in
+    row-major order) against the exact-rational rule: (disagreements that are
+    not near ties, near-tie disagreements)."""
+    p = oracle.quantize(x, block, rule)
     nib = unpack(p.codes)
     alpha = Fr(float(p.alpha))
     bad, ties = 0, 0
-    for r in range(x.shape[0]):
-        for b in range(x.shape[1] // 16):
-            xs = [float(v) for v in x[r, b * 16:(b + 1) * 16]]
-            c, s, codes, e6, e4 = exact_block(xs, alpha, rule == FOUR_OVER_SIX)
-            got_s = Fr(oracle.e4m3_value(int(p.scales[r, b])))
-            got_c = [int(v) & 7 for v in nib[r, b * 16:(b + 1) * 16]]
-            want_c = [v & 7 for v in codes]
-            if got_s != s or got_c != want_c:
-                m = max(abs(v) for v in xs)
-                if _near_tie(xs, alpha, m):
-                    ties += 1
-                else:
-                    bad += 1
+    if block == ROW16:
+        blocks = [((r, b), (slice(r, r + 1), slice(b * 16, (b + 1) * 16)))
+                  for r in range(x.shape[0]) for b in range(x.shape[1] // 16)]
+    else:
+        blocks = [((rb, cb), (slice(rb * 16, (rb + 1) * 16), slice(cb * 16, (cb + 1) * 16)))
+                  for rb in range(x.shape[0] // 16) for cb in range(x.shape[1] // 16)]
+    for sidx, sl in blocks:
+        xs = [float(v) for v in x[sl].ravel()]
+        c, s, codes, e6, e4 = exact_block(xs, alpha, rule == FOUR_OVER_SIX)
+        got_s = Fr(oracle.e4m3_value(int(p.scales[sidx])))
+        got_c = [int(v) & 7 for v in nib[sl].ravel()]
+        want_c = [v & 7 for v in codes]
+        if got_s != s or got_c != want_c:
+            m = max(abs(v) for v in xs)
+            if _near_tie(xs, alpha, m):
+                ties += 1
+            else:
+                bad += 1
     return bad, ties
 
 
@@ -328,6 +336,61 @@ def test_exact_rational_two_value_family():
             # midpoint that the fp32 reciprocal lands on the other side of
             mids = [(E2M1[j] + E2M1[j + 1]) / 2 for j in range(7)]
             assert e4 == e6 or v4 in mids, (float(y), got, want)
+
+
+def test_exact_rational_tile16_random_tiles():
+    # 16x16 weight tiles: one scale per 256 elements, the 6-vs-4 choice on the
+    # whole tile's squared error (NVFP4 training recipe: 2D weight blocks)
+    x = _rand(19, (64, 256), sigma=0.02)
+    bad, ties = _compare_exact(x, FOUR_OVER_SIX, TILE16)
+    assert bad == 0
+    assert ties <= 2
+    bad, ties = _compare_exact(x, STATIC6, TILE16)
+    assert bad == 0
+
+
+def test_exact_rational_tile16_small_alphabet_tiles():
+    rng = np.random.default_rng(20)
+    alphabet = np.arange(0, 49) / 8.0
+    x = rng.choice(alphabet, size=(48, 128)) * np.where(rng.random((48, 128)) < 0.5, -1, 1)
+    # per-tile magnitudes spread over many E4M3 binades
+    x = x * (2.0 ** rng.integers(-8, 6, (3, 8))).repeat(16, axis=0).repeat(16, axis=1)
+    x[0, 0] = 2688.0
+    x = x.astype(np.float32)
+    bad, ties = _compare_exact(x, FOUR_OVER_SIX, TILE16)
+    assert bad == 0
+
+
+def test_exact_rational_tile16_two_value_family():
+    # tile {6 at (0, 0), y at (7, 9), 0 elsewhere} with alpha = 1: the tile's
+    # squared error is that of the two values, so the exact rule picks the
+    # 4-candidate (scale 1.5, byte 0x3C) iff y's error under 1.5 is smaller
+    ys = np.unique(np.concatenate([np.linspace(0.01, 6, 97), np.arange(1, 49) / 8.0])).astype(np.float32)
+    x = np.zeros((16, 16 * (len(ys) + 1)), np.float32)
+    for i, y in enumerate(ys):
+        x[0, 16 * i] = 6.0
+        x[7, 16 * i + 9] = y
+    x[3, -1] = 2688.0
+    p = oracle.quantize(x, TILE16, FOUR_OVER_SIX)
+    assert p.alpha == 1.0
+    mids = [(E2M1[j] + E2M1[j + 1]) / 2 for j in range(7)]
+    for i, y in enumerate(ys):
+        yy = Fr(float(y))
+        e6 = (yy - E2M1[min(range(8), key=lambda j: (abs(yy - E2M1[j]), j % 2))]) ** 2
+        v4 = yy / Fr(3, 2)
+        e4 = (yy - Fr(3, 2) * E2M1[min(range(8), key=lambda j: (abs(v4 - E2M1[j]), j % 2))]) ** 2
+        want = 0x3C if e4 < e6 else 0x38
+        got = int(p.scales[0, i])
+        if got != want:
+            assert e4 == e6 or v4 in mids, (float(y), got, want)
+    # the same pairs as 1x16 blocks decide the same way (the zeros add no error)
+    r = np.zeros((len(ys), 16), np.float32)
+    r[:, 0] = 6.0
+    r[:, 9] = ys
+    r = np.concatenate([r, np.full((1, 16), 0, np.float32)])
+    r[-1, 0] = 2688.0
+    q = oracle.quantize(r, ROW16, FOUR_OVER_SIX)
+    assert np.array_equal(q.scales[:-1, 0], p.scales[0, :-1])
 
 
 def test_exact_reading_diagnostic_rate():
