@@ -328,26 +328,22 @@ def _bf16_or_f32(x: np.ndarray) -> np.ndarray:
 
 def bf16_rne_f64(y: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (nearest, ties to even) in one step: the
-    exact bf16 neighbours of each value are compared in fp64."""
+    magnitude's bf16 neighbours are compared with |y| exactly in fp64 and the
+    sign is put back (subnormal bf16 values included; magnitudes below half
+    the smallest subnormal give a signed zero)."""
     y = np.asarray(y, np.float64)
-    f = y.astype(np.float32)                       # may round; corrected below
-    bits = f.view(np.uint32).astype(np.int64)
-    lo = (bits & ~0xFFFF) & 0xFFFFFFFF             # bf16 truncation of f (toward zero in magnitude)
-    cand = []
-    for d in (-0x10000, 0, 0x10000, 0x20000):
-        c = (lo + d) & 0xFFFFFFFF
-        cand.append(c)
-    cand = np.stack(cand)
-    vals = cand.astype(np.uint32).view(np.float32).astype(np.float64)
-    err = np.abs(vals - y[None])
-    best = np.argmin(err, axis=0)
-    # ties: prefer the candidate with an even bf16 mantissa
-    out = np.take_along_axis(cand, best[None], axis=0)[0]
-    e_best = np.take_along_axis(err, best[None], axis=0)[0]
-    for k in range(4):
-        tie = (err[k] == e_best) & (((cand[k] >> 16) & 1) == 0) & (cand[k] != out)
-        out = np.where(tie, cand[k], out)
-    return (out >> 16).astype(np.uint16)
+    sign = np.where(np.signbit(y), 0x8000, 0).astype(np.int64)
+    a = np.abs(y)
+    t = (a.astype(np.float32).view(np.uint32).astype(np.int64) >> 16)   # near |y|'s bf16 pattern
+    cand = np.stack([t + d for d in (-2, -1, 0, 1, 2)])
+    cand = np.clip(cand, 0, 0x7F80)                                     # magnitudes only: 0 ... inf
+    vals = (cand.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(vals - a[None])
+    best_err = err.min(axis=0)
+    # among the nearest candidates take the one with an even bf16 pattern
+    pick = np.where((err == best_err[None]) & ((cand & 1) == 0), cand, -1).max(axis=0)
+    pick = np.where(pick < 0, np.take_along_axis(cand, err.argmin(axis=0)[None], axis=0)[0], pick)
+    return (sign | pick).astype(np.uint16)
 
 
 _bf16_rne_f64 = bf16_rne_f64

@@ -135,17 +135,18 @@ def test_sampled_matches_full():
 
 
 def _bf16_brute(y: float) -> int:
-    """Nearest bf16 (ties to even mantissa) of a double, by search."""
-    f = np.float32(y)
-    b = int(np.array([f]).view(np.uint32)[0]) & ~0xFFFF
+    """Nearest bf16 (ties to even mantissa) of a double, by search over the
+    bf16 magnitudes next to |y|; the sign bit is that of y."""
+    sign = 0x8000 if np.signbit(y) else 0
+    a = abs(float(y))
+    t = int(np.array([np.float32(a)]).view(np.uint32)[0]) >> 16
     best = None
-    for d in range(-3, 4):
-        c = (b + d * 0x10000) & 0xFFFFFFFF
-        v = float(np.array([c], np.uint32).view(np.float32)[0])
-        key = (abs(v - y), (c >> 16) & 1)
+    for c in range(max(0, t - 3), min(t + 4, 0x7F81)):
+        v = float(np.array([c << 16], np.uint32).view(np.float32)[0])
+        key = (abs(v - a), c & 1)
         if best is None or key < best[0]:
-            best = (key, c >> 16)
-    return best[1]
+            best = (key, c)
+    return sign | best[1]
 
 
 def test_bf16_rounding_of_doubles():
@@ -155,6 +156,17 @@ def test_bf16_rounding_of_doubles():
     got = oracle._bf16_rne_f64(y)
     assert list(got[:4]) == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
     assert np.array_equal(got, np.array([_bf16_brute(v) for v in y], np.uint16))
+    # the subnormal range and below: the smallest bf16 subnormal is 2^-133;
+    # 2^-134 is the midpoint between it and zero (ties to the even zero)
+    tiny = np.array([2.0 ** -134, 2.0 ** -134 * (1 + 2.0 ** -20), -2.0 ** -134, 2.0 ** -133, 3 * 2.0 ** -134,
+                     2.0 ** -126, 2.0 ** -127 * 1.5, 1e-45, -1e-45, 1e-80, -1e-80, 0.0, -0.0, 2.0 ** -140])
+    want = [0x0000, 0x0001, 0x8000, 0x0001, 0x0002, 0x0080, 0x0060, 0x0000, 0x8000, 0x0000, 0x8000, 0x0000,
+            0x8000, 0x0000]
+    assert list(oracle._bf16_rne_f64(tiny)) == want
+    assert [_bf16_brute(v) for v in tiny] == want
+    rng2 = np.random.default_rng(54)
+    small = rng2.standard_normal(3000) * 2.0 ** rng2.uniform(-140, -120, 3000)
+    assert np.array_equal(oracle._bf16_rne_f64(small), np.array([_bf16_brute(v) for v in small], np.uint16))
 
 
 def test_bf16_rne_of_floats():
