@@ -47,8 +47,10 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never allocates or frees device memory and keeps no state
- *     between calls.  Work is enqueued on `stream` (0 = null stream) and is
- *     asynchronous; buffers must stay alive until the stream reaches it.
+ *     between calls, except the static scratch array of
+ *     nvfp4_linear_no_alloc (see there).  Work is enqueued on `stream`
+ *     (0 = null stream) and is asynchronous; buffers must stay alive until
+ *     the stream reaches it.
  *   - Inputs must not alias outputs or the workspace.
  *   - Arguments are validated before anything is enqueued; on any error
  *     nothing is enqueued and outputs are untouched.  Launch failures are
@@ -91,7 +93,9 @@ typedef enum {
     NVFP4_ERR_ALIGN = 3,       /* pointer or leading dimension misaligned */
     NVFP4_ERR_DTYPE = 4,       /* unknown dtype / block / rule enum value */
     NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-    NVFP4_ERR_LAUNCH = 6       /* a kernel launch failed (hipGetLastError) */
+    NVFP4_ERR_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError) */
+    NVFP4_ERR_SCRATCH = 7      /* nvfp4_linear_no_alloc: the call needs more than
+                                  NVFP4_NO_ALLOC_SCRATCH_BYTES of scratch */
 } nvfp4_status_t;
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype_t;
@@ -199,6 +203,33 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
                             int w_scale_layout, int64_t n,
                             void *y, int y_dtype, int64_t ldy, float *y_amax,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_linear_no_alloc -- nvfp4_linear for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, kernels and results, with
+ * the workspace taken from a static device array inside the library instead
+ * of a caller buffer.  The call itself allocates nothing (no hipMalloc, no
+ * allocating library routine).
+ *   Scratch: NVFP4_NO_ALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ *   first call on that GPU until the process ends; the call uses the copy of
+ *   the CURRENT device (the stream must belong to it).  A call needing more,
+ *   i.e. nvfp4_linear_workspace_size(m, k) > NVFP4_NO_ALLOC_SCRATCH_BYTES
+ *   (about 119 M activation elements, e.g. 32768 x 3072 fits), returns
+ *   NVFP4_ERR_SCRATCH and enqueues nothing.
+ *   Every call on a GPU shares that GPU's scratch and leaves its contents
+ *   there: calls that can overlap on one GPU (two streams, two host threads
+ *   without ordering) RACE and must be serialized by the caller.
+ *   The first call on a device looks the array's address up
+ *   (hipGetSymbolAddress); a failure there returns NVFP4_ERR_LAUNCH.
+ * Other arguments, checks and errors as nvfp4_linear.
+ */
+#define NVFP4_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+nvfp4_status_t nvfp4_linear_no_alloc(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                     int w_scale_layout, int64_t n,
+                                     void *y, int y_dtype, int64_t ldy, float *y_amax, hipStream_t stream);
 
 /*
  * nvfp4_linear_lora -- the W4A4 linear with a BF16 LoRA branch:

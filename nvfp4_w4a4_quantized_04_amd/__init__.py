@@ -29,7 +29,8 @@ SCALE_1D, SCALE_2D = 0, 1
 _BLOCKS = {"row16": ROW16, "tile16": TILE16, "col16": COL16}
 _RULES = {"static6": STATIC6, "static_6": STATIC6, "4over6": FOUR_OVER_SIX, "mse": FOUR_OVER_SIX}
 
-STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "alignment", 4: "dtype/enum", 5: "workspace", 6: "launch"}
+STATUS = {0: "ok", 1: "null pointer", 2: "shape", 3: "alignment", 4: "dtype/enum", 5: "workspace", 6: "launch",
+          7: "larger than the no-allocation scratch"}
 
 
 class NVFP4Error(RuntimeError):
@@ -89,6 +90,8 @@ def _load():
     L.nvfp4_quantize_col16_rht.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_transpose_tile16.restype = i32
     L.nvfp4_transpose_tile16.argtypes = [P, P, P, i64, i64, P, P, P, P]
+    L.nvfp4_linear_no_alloc.restype = i32
+    L.nvfp4_linear_no_alloc.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, P]
     return L
 
 
@@ -99,7 +102,9 @@ EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspac
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
             "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",
             "nvfp4_kv_dequantize_window", "nvfp4_linear_lora",
-            "nvfp4_linear_lora_workspace_size"]
+            "nvfp4_linear_lora_workspace_size", "nvfp4_linear_no_alloc"]
+
+NO_ALLOC_SCRATCH_BYTES = 64 << 20      # NVFP4_NO_ALLOC_SCRATCH_BYTES
 
 
 def _check(fn: str, st: int):
@@ -332,6 +337,29 @@ def linear(x: torch.Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, rule="4ove
         _ptr(x), _dtype_code(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n,
         _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _ptr(workspace), workspace.numel(),
         _stream()))
+    return out
+
+
+def linear_no_alloc(x: torch.Tensor, w: NVFP4Tensor, out: torch.Tensor, rule="4over6",
+                    amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_linear_no_alloc: the same W4A4 forward as `linear`, with the
+    workspace taken from the library's static per-GPU scratch (no device
+    allocation in the call; calls on one GPU must not overlap).  `out` is
+    required, so the call allocates nothing on this side either."""
+    _need_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2D with unit column stride")
+    cw, sw, aw, lw, n, kw = w.operand()
+    m, k = x.shape
+    if k != kw:
+        raise ValueError(f"in_features mismatch {k} vs {kw}")
+    _check_packed(w, w.rows, w.cols, w.block, "w")
+    _check_out(out, (m, n))
+    _check_vec(amax_out, 1, torch.float32, "amax_out")
+    _need_gpu(cw, sw, aw, out, amax_out)
+    _check("nvfp4_linear_no_alloc", lib.nvfp4_linear_no_alloc(
+        _ptr(x), _dtype_code(x), m, k, x.stride(0), _rule(rule), _ptr(cw), _ptr(sw), _ptr(aw), lw, n,
+        _ptr(out), _out_dtype_code(out.dtype), out.stride(0), _ptr(amax_out), _stream()))
     return out
 
 

@@ -2,6 +2,8 @@
 // Every entry point validates everything before enqueueing anything.
 #include <nvfp4.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace nvfp4;
@@ -115,6 +117,7 @@ const char *nvfp4_status_string(nvfp4_status_t s)
     case NVFP4_ERR_DTYPE: return "invalid dtype, block or rule";
     case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    case NVFP4_ERR_SCRATCH: return "call needs more than the static scratch of the no-allocation entry point";
     }
     return "unknown status";
 }
@@ -207,10 +210,14 @@ size_t nvfp4_linear_workspace_size(int64_t m, int64_t k)
            round_up((size_t)(m * k / 16), kAlignWs);
 }
 
-nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
-                            const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
-                            int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, float *y_amax,
-                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// The argument checks of nvfp4_linear other than the workspace's.
+nvfp4_status_t check_linear_args(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                                 const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                 int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, float *y_amax)
 {
     if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype) || !rule_ok(rule) ||
         (w_scale_layout != NVFP4_SCALE_1D && w_scale_layout != NVFP4_SCALE_2D))
@@ -224,11 +231,16 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
         (y_amax && ((uintptr_t)y_amax & 3u) != 0) ||
         (w_codes && !aligned16(w_codes)) || (w_scales && !aligned16(w_scales)))
         return NVFP4_ERR_ALIGN;
-    if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
-        return NVFP4_ERR_WORKSPACE;
-    if (((uintptr_t)workspace % kAlignWs) != 0)
-        return NVFP4_ERR_ALIGN;
-    uint8_t *ws = (uint8_t *)workspace;
+    return NVFP4_OK;
+}
+
+// The launches of nvfp4_linear on a checked, large enough workspace ws
+// (device memory, 256-byte aligned): amax partials, activation quantize, GEMM.
+nvfp4_status_t linear_launches(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                               const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                               int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, float *y_amax,
+                               uint8_t *ws, hipStream_t stream)
+{
     float *alpha = (float *)ws;
     float *partials = (float *)(ws + kAlignWs);
     uint8_t *codes = ws + kAlignWs + round_up(kAmaxBytes, kAlignWs);
@@ -240,6 +252,82 @@ nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, in
     GemmOperand A{codes, scales, alpha, NVFP4_SCALE_1D};
     GemmOperand B{w_codes, w_scales, w_alpha, w_scale_layout};
     return launch_status(launch_gemm(A, B, m, n, k, y, y_dtype, ldy, y_amax, stream));
+}
+
+// Scratch of nvfp4_linear_no_alloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code its name
+// is only a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static_assert(NVFP4_NO_ALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[NVFP4_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t *g_scratch_ptr[kMaxScratchDevices];     // device address of `scratch` on each device, once looked up
+
+// The current device's copy of the scratch array (its address looked up on
+// the first call on that device).
+nvfp4_status_t current_device_scratch(uint8_t **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+        (void)hipGetLastError();
+        return NVFP4_ERR_LAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();            // leave no sticky error for the caller's next call
+            return NVFP4_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = (uint8_t *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status_t nvfp4_linear(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                            const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                            int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy, float *y_amax,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    nvfp4_status_t st = check_linear_args(x, x_dtype, m, k, ldx, rule, w_codes, w_scales, w_alpha, w_scale_layout,
+                                          n, y, y_dtype, ldy, y_amax);
+    if (st != NVFP4_OK)
+        return st;
+    if (!workspace || workspace_bytes < nvfp4_linear_workspace_size(m, k))
+        return NVFP4_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlignWs) != 0)
+        return NVFP4_ERR_ALIGN;
+    return linear_launches(x, x_dtype, m, k, ldx, rule, w_codes, w_scales, w_alpha, w_scale_layout, n, y, y_dtype,
+                           ldy, y_amax, (uint8_t *)workspace, stream);
+}
+
+nvfp4_status_t nvfp4_linear_no_alloc(const void *x, int x_dtype, int64_t m, int64_t k, int64_t ldx, int rule,
+                                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_alpha,
+                                     int w_scale_layout, int64_t n, void *y, int y_dtype, int64_t ldy,
+                                     float *y_amax, hipStream_t stream)
+{
+    nvfp4_status_t st = check_linear_args(x, x_dtype, m, k, ldx, rule, w_codes, w_scales, w_alpha, w_scale_layout,
+                                          n, y, y_dtype, ldy, y_amax);
+    if (st != NVFP4_OK)
+        return st;
+    if (nvfp4_linear_workspace_size(m, k) > (size_t)NVFP4_NO_ALLOC_SCRATCH_BYTES)
+        return NVFP4_ERR_SCRATCH;
+    uint8_t *ws = nullptr;
+    st = current_device_scratch(&ws);
+    if (st != NVFP4_OK)
+        return st;
+    // nothing in the scratch has to start at zero: the amax pass writes every
+    // partial the quantizer reads, the quantizer writes alpha, codes and scales
+    return linear_launches(x, x_dtype, m, k, ldx, rule, w_codes, w_scales, w_alpha, w_scale_layout, n, y, y_dtype,
+                           ldy, y_amax, ws, stream);
 }
 
 size_t nvfp4_linear_lora_workspace_size(int64_t m, int64_t k, int rank)

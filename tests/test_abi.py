@@ -34,8 +34,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     import nvfp4_w4a4_quantized_04_amd as m
-    for st in range(7):
+    for st in range(8):
         assert m.lib.nvfp4_status_string(st)
+    assert b"scratch" in m.lib.nvfp4_status_string(7)
 
 
 FAKE = 1 << 20          # an aligned non-null address that is never dereferenced
