@@ -174,16 +174,19 @@ struct Producer {
     }
 };
 
+// MFMA fragments of substep s: the wave's first A and B fragment offsets in
+// the stage buffer plus constant strides (32 LDS rows per fragment), so the
+// offsets live in two registers and the rest are instruction immediates.
 template <int TM, int TN>
-__device__ __forceinline__ void read_frags(const uint8_t *stage, const int (&a_frag)[TM], const int (&b_frag)[TN],
-                                           int s, half8v (&af)[TM], half8v (&bf)[TN])
+__device__ __forceinline__ void read_frags(const uint8_t *stage, int a_frag, int b_frag, int s, half8v (&af)[TM],
+                                           half8v (&bf)[TN])
 {
 #pragma unroll
     for (int i = 0; i < TM; i++)
-        af[i] = *reinterpret_cast<const half8v *>(stage + a_frag[i] + s * 32);
+        af[i] = *reinterpret_cast<const half8v *>(stage + a_frag + i * 32 * kLdsRow + s * 32);
 #pragma unroll
     for (int j = 0; j < TN; j++)
-        bf[j] = *reinterpret_cast<const half8v *>(stage + b_frag[j] + s * 32);
+        bf[j] = *reinterpret_cast<const half8v *>(stage + b_frag + j * 32 * kLdsRow + s * 32);
 }
 
 // Row pitch of the bf16 C tile staged in LDS for the epilogue (16 bytes of
@@ -344,14 +347,10 @@ void k_gemm_nvfp4(GemmArgs g)
         for (int j = 0; j < TN; j++)
             acc[i][j] = float16v{};
 
-    // fragment of MFMA tile i: LDS row (tile row + lane%32), k half (lane/32)
-    int a_frag[TM], b_frag[TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++)
-        a_frag[i] = (wm * 32 * TM + i * 32 + l32) * kLdsRow + half * 16;
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-        b_frag[j] = (BM + wn * 32 * TN + j * 32 + l32) * kLdsRow + half * 16;
+    // fragment of MFMA tile i: LDS row (tile row + lane%32), k half (lane/32);
+    // tile i adds i * 32 rows to the first one
+    const int a_frag = (wm * 32 * TM + l32) * kLdsRow + half * 16;
+    const int b_frag = (BM + wn * 32 * TN + l32) * kLdsRow + half * 16;
 
     __syncthreads();
     half8v af[2][TM], bf[2][TN];
@@ -393,6 +392,19 @@ void k_gemm_nvfp4(GemmArgs g)
         }
     }
 
+    // The lane's coordinates after the loop, recovered from the fragment
+    // offsets, which are live through the main loop anyway (keeping the wave
+    // and lane indices themselves alive across the loop costs registers the
+    // loop does not have): arow = wm*32*TM + l32, brow = BM + wn*32*TN + l32,
+    // ehalf = lane / 32.
+    // The empty asm makes the offsets opaque, so the compiler derives the
+    // coordinates from them here instead of keeping the index arithmetic of
+    // the loop set-up alive through the loop.
+    int af0 = a_frag, bf0 = b_frag;
+    asm volatile("" : "+v"(af0), "+v"(bf0));
+    const int arow = af0 / kLdsRow;
+    const int ehalf = (af0 - arow * kLdsRow) >> 4;
+    const int brow = bf0 / kLdsRow;
     float scale = *g.a_alpha * *g.b_alpha;
     if (LORA) {
         // C = scale_q * acc + lora_scale * U B^T, accumulated as
@@ -406,19 +418,35 @@ void k_gemm_nvfp4(GemmArgs g)
         scale = g.lora_scale;
         __syncthreads();                                  // the producers staged U and B
         const int pr = lora_row_bytes(g.lora_r);
-        const uint8_t *ua_base = lds + (wm * 32 * TM + l32) * pr + half * 16;
-        const uint8_t *ub_base = lds + (BM + wn * 32 * TN + l32) * pr + half * 16;
+        const uint8_t *ua_base = lds + arow * pr + ehalf * 16;
+        const uint8_t *ub_base = lds + brow * pr + ehalf * 16;
         for (int kk = 0; kk < g.lora_r; kk += 16) {
-            bf16x8v ua[TM];
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-                ua[i] = *reinterpret_cast<const bf16x8v *>(ua_base + i * 32 * pr + kk * 2);
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const bf16x8v ub = *reinterpret_cast<const bf16x8v *>(ub_base + j * 32 * pr + kk * 2);
+            // hold the fragments of the shorter side in registers (fewer live
+            // registers next to the accumulators), stream the other side
+            if constexpr (TM <= TN) {
+                bf16x8v ua[TM];
 #pragma unroll
                 for (int i = 0; i < TM; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, ua[i], acc[i][j], 0, 0, 0);
+                    ua[i] = *reinterpret_cast<const bf16x8v *>(ua_base + i * 32 * pr + kk * 2);
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const bf16x8v ub = *reinterpret_cast<const bf16x8v *>(ub_base + j * 32 * pr + kk * 2);
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, ua[i], acc[i][j], 0, 0, 0);
+                }
+            } else {
+                bf16x8v ub[TN];
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    ub[j] = *reinterpret_cast<const bf16x8v *>(ub_base + j * 32 * pr + kk * 2);
+#pragma unroll
+                for (int i = 0; i < TM; i++) {
+                    const bf16x8v ua = *reinterpret_cast<const bf16x8v *>(ua_base + i * 32 * pr + kk * 2);
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub[j], ua, acc[i][j], 0, 0, 0);
+                }
             }
         }
     }
@@ -430,13 +458,8 @@ void k_gemm_nvfp4(GemmArgs g)
         if (LORA)
             __syncthreads();          // every wave has read its U and B fragments: LDS is free
         // bf16 tile into the (now idle) stage buffers, then all eight waves
-        // write whole rows with 16-byte stores.  The lane's coordinates are
-        // recovered from the fragment offsets, which are live through the
-        // main loop anyway (keeping the thread index itself alive across the
-        // loop costs registers the loop does not have).
-        const int arow = a_frag[0] / kLdsRow;                  // wm*32*TM + l32
-        const int ehalf = (a_frag[0] - arow * kLdsRow) >> 4;
-        const int bcol0 = b_frag[0] / kLdsRow - BM - (arow & 31);   // wn*32*TN
+        // write whole rows with 16-byte stores
+        const int bcol0 = brow - BM - (arow & 31);                 // wn*32*TN
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const int lrow = arow + i * 32;
@@ -466,14 +489,14 @@ void k_gemm_nvfp4(GemmArgs g)
     } else {
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int row = m0 + wm * 32 * TM + i * 32 + l32;
+        const int row = m0 + arow + i * 32;
         if (row >= g.M)
             continue;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const int col = n0 + wn * 32 * TN + j * 32 + 8 * q + 4 * half;
+                const int col = n0 + (brow - BM - (arow & 31)) + j * 32 + 8 * q + 4 * ehalf;
                 const float v0 = acc[i][j][4 * q + 0] * scale, v1 = acc[i][j][4 * q + 1] * scale;
                 const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
                 const int64_t off = (int64_t)row * g.ldc + col;
