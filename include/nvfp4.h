@@ -268,12 +268,18 @@ size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in);
 /*
  * nvfp4_wgrad -- weight gradient dW[n][k] = sum_t dY[t][n] * X[t][k] with
  * both operands quantized in 16-blocks along the token axis (NVFP4_COL16,
- * `rule`, amax of each computed on the device).  dy [tokens][n_out] (ld lddy),
- * x [tokens][k_in] (ld ldx), same dtype; tokens % 16 == 0.  dW [n_out][k_in]
- * (ld lddw), fp32 or bf16.
+ * `rule`).  dy [tokens][n_out] (ld lddy), x [tokens][k_in] (ld ldx), same
+ * dtype; tokens % 16 == 0.  dW [n_out][k_in] (ld lddw), fp32 or bf16.
  * rht_signs: -1 quantizes dY and X as they are; 0..0xFFFF first applies the
  * random Hadamard transform with these signs to both, along the tokens (see
  * nvfp4_quantize_col16_rht), so dW is computed from R dY and R X.
+ * dy_amax, x_amax (optional, device, 4-byte aligned): the operands' max |.|,
+ * each replacing that operand's amax pass (one read of the operand fewer).
+ * The COL16 packing of X shares its global scale with the forward's ROW16
+ * packing of the same X (same amax): hand in the amax the forward used,
+ * e.g. the y_amax / c_amax output of the GEMM that produced X, or of the one
+ * that produced dY.  With the transform the amax must be that of R dY / R X.
+ * NULL: computed on the device.
  * Source: "The three GEMMs of backpropagation" (WGRAD: activation x output
  * gradient -> weight gradient) with 1D gradient blocks along the reduction
  * dimension ("NVFP4 training recipe"), and "Random Hadamard Transform (RHT)
@@ -281,6 +287,7 @@ size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in);
  */
 nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out,
                            int64_t k_in, int64_t lddy, int64_t ldx, int rule, int rht_signs,
+                           const float *dy_amax, const float *x_amax,
                            void *dw, int dw_dtype, int64_t lddw,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -326,6 +333,53 @@ nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows
 nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *alpha,
                                       int64_t rows, int64_t cols, uint8_t *codes_t, uint8_t *scales_t,
                                       float *alpha_t, hipStream_t stream);
+
+/* ---------------------------------------- KV cache, one scale per chunk */
+
+/* Workspace of nvfp4_kv_quantize_chunked (per-chunk amax partial maxima):
+ * 4 KiB per chunk. */
+size_t nvfp4_kv_chunked_workspace_size(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk);
+
+/*
+ * nvfp4_kv_quantize_chunked -- the KV quantizer with one FP32 global scale
+ * per CHUNK of tokens, all chunks in one call (two launches: the per-chunk
+ * amax partials, then the quantizer; one launch when chunk_amax is given).
+ *   kv [heads][tokens][head_dim] (contiguous, 16-byte aligned, fp32 or
+ *   bf16); chunk c holds tokens [c * tokens_per_chunk, min((c + 1) *
+ *   tokens_per_chunk, tokens)) of every head, n_chunks = ceil(tokens /
+ *   tokens_per_chunk).  Each chunk is quantized exactly as nvfp4_kv_quantize
+ *   would quantize that chunk alone (16-blocks along head_dim, `rule`).
+ *   codes [heads][tokens][head_dim/2], scales [heads][tokens][head_dim/16]:
+ *   the ROW16 packing of the [heads * tokens][head_dim] view.
+ *   alphas [n_chunks] (fp32, device): chunk c's global scale.
+ *   chunk_amax: NULL (computed, one extra read of the tensor) or a device
+ *   array [n_chunks] of the chunks' max |x|.
+ *   1 <= heads <= 1024, head_dim % 16 == 0 and >= 16, tokens_per_chunk >= 1,
+ *   n_chunks <= 65535; tokens == 0 enqueues nothing.
+ *   workspace >= nvfp4_kv_chunked_workspace_size() (unused with chunk_amax).
+ * Source: "Chunkwise quantization procedure" (a per-chunk, per-layer FP32
+ * global scale for the keys and values of each chunk) and "KV cache
+ * quantization" (16-element blocks along the head dimension), NVFP4 Inference
+ * section of the architecture walkthrough page; the paper-notes page gives
+ * the chunk size (8 latent frames).
+ */
+nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t heads, int64_t tokens,
+                                         int64_t head_dim, int64_t tokens_per_chunk, int rule,
+                                         const float *chunk_amax, uint8_t *codes, uint8_t *scales,
+                                         float *alphas, void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
+ * nvfp4_kv_dequantize_chunked -- y = (q * s) * alpha_c for a tensor packed by
+ * nvfp4_kv_quantize_chunked with the same (heads, tokens, head_dim,
+ * tokens_per_chunk): alpha_c the scale of the element's chunk.  y
+ * [heads][tokens][head_dim], contiguous, 16-byte aligned, fp32 or bf16
+ * (round to nearest even).
+ * Source: the "Hierarchical scaling" equation with the per-chunk scale.
+ */
+nvfp4_status_t nvfp4_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
+                                           int64_t heads, int64_t tokens, int64_t head_dim,
+                                           int64_t tokens_per_chunk, void *y, int y_dtype, hipStream_t stream);
 
 /* ------------------------------------------------ KV cache, consumer side */
 

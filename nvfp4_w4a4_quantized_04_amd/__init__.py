@@ -74,7 +74,7 @@ def _load():
     L.nvfp4_wgrad_workspace_size.restype = sz
     L.nvfp4_wgrad_workspace_size.argtypes = [i64, i64, i64]
     L.nvfp4_wgrad.restype = i32
-    L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, i32, P, i32, i64, P, sz, P]
+    L.nvfp4_wgrad.argtypes = [P, P, i32, i64, i64, i64, i64, i64, i32, i32, P, P, P, i32, i64, P, sz, P]
     L.nvfp4_kv_smooth_workspace_size.restype = sz
     L.nvfp4_kv_smooth_workspace_size.argtypes = [i64, i64]
     L.nvfp4_kv_quantize_smoothed.restype = i32
@@ -90,6 +90,12 @@ def _load():
     L.nvfp4_quantize_col16_rht.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_transpose_tile16.restype = i32
     L.nvfp4_transpose_tile16.argtypes = [P, P, P, i64, i64, P, P, P, P]
+    L.nvfp4_kv_chunked_workspace_size.restype = sz
+    L.nvfp4_kv_chunked_workspace_size.argtypes = [i64, i64, i64, i64]
+    L.nvfp4_kv_quantize_chunked.restype = i32
+    L.nvfp4_kv_quantize_chunked.argtypes = [P, i32, i64, i64, i64, i64, i32, P, P, P, P, P, sz, P]
+    L.nvfp4_kv_dequantize_chunked.restype = i32
+    L.nvfp4_kv_dequantize_chunked.argtypes = [P, P, P, i64, i64, i64, i64, P, i32, P]
     L.nvfp4_linear_no_alloc.restype = i32
     L.nvfp4_linear_no_alloc.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, P]
     return L
@@ -102,7 +108,8 @@ EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspac
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
             "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",
             "nvfp4_kv_dequantize_window", "nvfp4_linear_lora",
-            "nvfp4_linear_lora_workspace_size", "nvfp4_linear_no_alloc"]
+            "nvfp4_linear_lora_workspace_size", "nvfp4_linear_no_alloc", "nvfp4_kv_chunked_workspace_size",
+            "nvfp4_kv_quantize_chunked", "nvfp4_kv_dequantize_chunked"]
 
 NO_ALLOC_SCRATCH_BYTES = 64 << 20      # NVFP4_NO_ALLOC_SCRATCH_BYTES
 
@@ -369,9 +376,12 @@ def wgrad_workspace(tokens: int, n_out: int, k_in: int, device="cuda") -> torch.
 
 def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4over6",
           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-          rht_signs: int | None = None) -> torch.Tensor:
+          rht_signs: int | None = None, dy_amax: torch.Tensor | None = None,
+          x_amax: torch.Tensor | None = None) -> torch.Tensor:
     """dW = dY^T X with both operands NVFP4-quantized along the token axis;
-    rht_signs (0..0xFFFF) first applies the random Hadamard transform to both."""
+    rht_signs (0..0xFFFF) first applies the random Hadamard transform to both.
+    dy_amax / x_amax (float32 [1] device tensors, optional): the operands' max
+    |.| (e.g. the forward's), replacing their amax passes."""
     _need_gpu(dy, x)
     t, n = dy.shape
     t2, k = x.shape
@@ -382,13 +392,15 @@ def wgrad(dy: torch.Tensor, x: torch.Tensor, out_dtype=torch.float32, rule="4ove
     if out is None:
         out = torch.empty((n, k), dtype=out_dtype, device=x.device)
     _check_out(out, (n, k))
+    _check_vec(dy_amax, 1, torch.float32, "dy_amax")
+    _check_vec(x_amax, 1, torch.float32, "x_amax")
     if workspace is None:
         workspace = wgrad_workspace(t, n, k, x.device)
-    _need_gpu(out, workspace)
+    _need_gpu(out, workspace, dy_amax, x_amax)
     _check("nvfp4_wgrad", lib.nvfp4_wgrad(
         _ptr(dy), _ptr(x), _dtype_code(x), t, n, k, dy.stride(0), x.stride(0), _rule(rule),
-        -1 if rht_signs is None else int(rht_signs), _ptr(out), _out_dtype_code(out.dtype), out.stride(0),
-        _ptr(workspace), workspace.numel(), _stream()))
+        -1 if rht_signs is None else int(rht_signs), _ptr(dy_amax), _ptr(x_amax), _ptr(out),
+        _out_dtype_code(out.dtype), out.stride(0), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
@@ -435,6 +447,65 @@ def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.T
         _ptr(x), _dtype_code(x), rows, cols, x.stride(0), _rule(rule), int(signs), _ptr(amax), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.alpha), _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
+    return out
+
+
+class KvChunked:
+    """A KV tensor [heads][tokens][head_dim] packed with one global scale per
+    chunk of tokens: codes [heads, tokens, d/2], scales [heads, tokens, d/16]
+    (uint8), alphas [n_chunks] (float32)."""
+
+    def __init__(self, codes, scales, alphas, heads, tokens, head_dim, tokens_per_chunk):
+        self.codes, self.scales, self.alphas = codes, scales, alphas
+        self.heads, self.tokens, self.head_dim, self.tokens_per_chunk = heads, tokens, head_dim, tokens_per_chunk
+
+
+def kv_quantize_chunked(kv: torch.Tensor, tokens_per_chunk: int, rule="4over6",
+                        out: KvChunked | None = None, chunk_amax: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> KvChunked:
+    """quantize_kv with the pages' per-chunk global scale: kv [heads, tokens,
+    head_dim] contiguous; chunk c = tokens [c*tpc, (c+1)*tpc) of every head.
+    chunk_amax (float32 [n_chunks], optional): the chunks' max |x|."""
+    _need_gpu(kv)
+    if kv.dim() != 3 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [heads, tokens, head_dim] tensor")
+    heads, tokens, d = kv.shape
+    tpc = int(tokens_per_chunk)
+    nch = (tokens + tpc - 1) // tpc if tpc > 0 else 0
+    if out is None:
+        dev = kv.device
+        out = KvChunked(torch.empty((heads, tokens, d // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((heads, tokens, d // 16), dtype=torch.uint8, device=dev),
+                        torch.empty(max(nch, 1), dtype=torch.float32, device=dev), heads, tokens, d, tpc)
+    if out.codes.shape != (heads, tokens, d // 2) or out.scales.shape != (heads, tokens, d // 16):
+        raise ValueError("output packed tensor has the wrong shape")
+    for t, what in ((out.codes, "codes"), (out.scales, "scales")):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous uint8")
+    _check_vec(out.alphas, nch, torch.float32, "alphas")
+    _check_vec(chunk_amax, nch, torch.float32, "chunk_amax")
+    if workspace is None:
+        workspace = torch.empty(lib.nvfp4_kv_chunked_workspace_size(heads, tokens, d, tpc), dtype=torch.uint8,
+                                device=kv.device)
+    _need_gpu(out.codes, out.scales, out.alphas, chunk_amax, workspace)
+    _check("nvfp4_kv_quantize_chunked", lib.nvfp4_kv_quantize_chunked(
+        _ptr(kv), _dtype_code(kv), heads, tokens, d, tpc, _rule(rule), _ptr(chunk_amax), _ptr(out.codes),
+        _ptr(out.scales), _ptr(out.alphas), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def kv_dequantize_chunked(t: KvChunked, dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """(q * s) * alpha of each element's chunk, [heads, tokens, head_dim]."""
+    _need_gpu(t.codes, t.scales, t.alphas)
+    shape = (t.heads, t.tokens, t.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=t.codes.device)
+    if tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [heads, tokens, head_dim] tensor")
+    _need_gpu(out)
+    _check("nvfp4_kv_dequantize_chunked", lib.nvfp4_kv_dequantize_chunked(
+        _ptr(t.codes), _ptr(t.scales), _ptr(t.alphas), t.heads, t.tokens, t.head_dim, t.tokens_per_chunk,
+        _ptr(out), _out_dtype_code(out.dtype), _stream()))
     return out
 
 

@@ -419,7 +419,8 @@ size_t nvfp4_wgrad_workspace_size(int64_t tokens, int64_t n_out, int64_t k_in)
 }
 
 nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tokens, int64_t n_out, int64_t k_in,
-                           int64_t lddy, int64_t ldx, int rule, int rht_signs, void *dw, int dw_dtype, int64_t lddw,
+                           int64_t lddy, int64_t ldx, int rule, int rht_signs, const float *dy_amax,
+                           const float *x_amax, void *dw, int dw_dtype, int64_t lddw,
                            void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!dtype_ok(dtype) || !dtype_ok(dw_dtype) || !rule_ok(rule) || !signs_ok(rht_signs))
@@ -430,7 +431,8 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
         return NVFP4_ERR_SHAPE;
     if ((n_out > 0 && k_in > 0 && !dw) || (tokens > 0 && ((n_out > 0 && !dy) || (k_in > 0 && !x))))
         return NVFP4_ERR_NULL;
-    if ((dy && !aligned_elem(dy, dtype)) || (x && !aligned_elem(x, dtype)) || (dw && !aligned_elem(dw, dw_dtype)))
+    if ((dy && !aligned_elem(dy, dtype)) || (x && !aligned_elem(x, dtype)) || (dw && !aligned_elem(dw, dw_dtype)) ||
+        ((uintptr_t)dy_amax & 3u) || ((uintptr_t)x_amax & 3u))
         return NVFP4_ERR_ALIGN;
     if (!workspace || workspace_bytes < nvfp4_wgrad_workspace_size(tokens, n_out, k_in))
         return NVFP4_ERR_WORKSPACE;
@@ -445,11 +447,12 @@ nvfp4_status_t nvfp4_wgrad(const void *dy, const void *x, int dtype, int64_t tok
     uint8_t *s_dy = c_dy + round_up((size_t)(n_out * tokens / 2), kAlignWs);
     uint8_t *c_x = s_dy + round_up((size_t)(n_out * tokens / 16), kAlignWs);
     uint8_t *s_x = c_x + round_up((size_t)(k_in * tokens / 2), kAlignWs);
-    nvfp4_status_t st = do_quantize(dy, dtype, tokens, n_out, lddy, NVFP4_COL16, rule, nullptr, c_dy, s_dy,
+    // a handed-in amax replaces that operand's amax pass
+    nvfp4_status_t st = do_quantize(dy, dtype, tokens, n_out, lddy, NVFP4_COL16, rule, dy_amax, c_dy, s_dy,
                                     alpha_dy, part_dy, stream, rht_signs);
     if (st != NVFP4_OK)
         return st;
-    st = do_quantize(x, dtype, tokens, k_in, ldx, NVFP4_COL16, rule, nullptr, c_x, s_x, alpha_x, part_x, stream,
+    st = do_quantize(x, dtype, tokens, k_in, ldx, NVFP4_COL16, rule, x_amax, c_x, s_x, alpha_x, part_x, stream,
                      rht_signs);
     if (st != NVFP4_OK)
         return st;
@@ -492,6 +495,79 @@ nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows
     }
     return do_quantize(x, x_dtype, rows, cols, ldx, NVFP4_COL16, rule, amax, codes, scales, alpha,
                        (float *)workspace, stream, rht_signs);
+}
+
+size_t nvfp4_kv_chunked_workspace_size(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk)
+{
+    (void)heads; (void)head_dim;
+    if (tokens <= 0 || tokens_per_chunk <= 0)
+        return kAlignWs;
+    const int64_t nch = (tokens + tokens_per_chunk - 1) / tokens_per_chunk;
+    return round_up((size_t)nch * kMaxAmaxSrc * sizeof(float), kAlignWs);
+}
+
+namespace {
+// The checks shared by the chunked KV quantize and dequantize.
+nvfp4_status_t check_kv_chunked(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk)
+{
+    if (heads < 1 || heads > kMaxAmaxSrc || tokens < 0 || head_dim < 16 || head_dim % 16 != 0 ||
+        tokens_per_chunk < 1 || tokens >= kMaxDim || head_dim >= kMaxDim || !lanes_fit(heads * tokens, head_dim))
+        return NVFP4_ERR_SHAPE;
+    const int64_t nch = (tokens + tokens_per_chunk - 1) / tokens_per_chunk;
+    const int64_t bpr = head_dim / 16;
+    // grid limits of the launches: chunks and quantize workgroups per segment
+    if (nch > 65535 || (tokens_per_chunk < tokens ? tokens_per_chunk : tokens) * bpr / kQuantThreads >= 0x7fffffff)
+        return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+}  // namespace
+
+nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t heads, int64_t tokens,
+                                         int64_t head_dim, int64_t tokens_per_chunk, int rule,
+                                         const float *chunk_amax, uint8_t *codes, uint8_t *scales, float *alphas,
+                                         void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!dtype_ok(kv_dtype) || !rule_ok(rule))
+        return NVFP4_ERR_DTYPE;
+    nvfp4_status_t st = check_kv_chunked(heads, tokens, head_dim, tokens_per_chunk);
+    if (st != NVFP4_OK)
+        return st;
+    if (tokens == 0)
+        return NVFP4_OK;                                  // no chunk, nothing to write
+    if (!kv || !codes || !scales || !alphas)
+        return NVFP4_ERR_NULL;
+    if (!aligned16(kv) || !aligned16(codes) || !aligned16(scales) || ((uintptr_t)alphas & 3u) ||
+        ((uintptr_t)chunk_amax & 3u))
+        return NVFP4_ERR_ALIGN;
+    if (!chunk_amax) {
+        if (!workspace || workspace_bytes < nvfp4_kv_chunked_workspace_size(heads, tokens, head_dim,
+                                                                            tokens_per_chunk))
+            return NVFP4_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return NVFP4_ERR_ALIGN;
+    }
+    return launch_status(launch_kv_quantize_chunked(kv, kv_dtype, heads, tokens, head_dim, tokens_per_chunk, rule,
+                                                    chunk_amax, codes, scales, alphas, (float *)workspace,
+                                                    stream));
+}
+
+nvfp4_status_t nvfp4_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
+                                           int64_t heads, int64_t tokens, int64_t head_dim,
+                                           int64_t tokens_per_chunk, void *y, int y_dtype, hipStream_t stream)
+{
+    if (!dtype_ok(y_dtype))
+        return NVFP4_ERR_DTYPE;
+    nvfp4_status_t st = check_kv_chunked(heads, tokens, head_dim, tokens_per_chunk);
+    if (st != NVFP4_OK)
+        return st;
+    if (tokens == 0)
+        return NVFP4_OK;
+    if (!codes || !scales || !alphas || !y)
+        return NVFP4_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(y) || ((uintptr_t)alphas & 3u))
+        return NVFP4_ERR_ALIGN;
+    return launch_status(launch_kv_dequantize_chunked(codes, scales, alphas, heads, tokens, head_dim,
+                                                      tokens_per_chunk, y, y_dtype, stream));
 }
 
 size_t nvfp4_kv_smooth_workspace_size(int64_t vectors, int64_t head_dim)

@@ -89,10 +89,11 @@ def test_gemm_and_linear_validation_without_gpu():
     assert need >= 32 * 64 * 9 // 16
     assert lin(FAKE, 1, 32, 64, 64, 1, FAKE, FAKE, FAKE, 1, 48, FAKE, 1, 48, None, FAKE + 16, need, None) == 3
     w = m.lib.nvfp4_wgrad
-    assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, -1, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
-    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, 0x10000, FAKE, 0, 32, FAKE, 1 << 30, None) == 4  # signs
-    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, -2, FAKE, 0, 32, FAKE, 1 << 30, None) == 4
-    assert w(FAKE, FAKE, 1, 1 << 23, 1 << 10, 32, 1 << 10, 32, 1, -1, FAKE, 0, 32, FAKE, 1 << 40, None) == 2
+    assert w(FAKE, FAKE, 1, 24, 32, 32, 32, 32, 1, -1, None, None, FAKE, 0, 32, FAKE, 1 << 30, None) == 2   # tokens % 16
+    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, 0x10000, None, None, FAKE, 0, 32, FAKE, 1 << 30, None) == 4  # signs
+    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, -2, None, None, FAKE, 0, 32, FAKE, 1 << 30, None) == 4
+    assert w(FAKE, FAKE, 1, 32, 32, 32, 32, 32, 1, -1, FAKE + 2, None, FAKE, 0, 32, FAKE, 1 << 30, None) == 3  # amax alignment
+    assert w(FAKE, FAKE, 1, 1 << 23, 1 << 10, 32, 1 << 10, 32, 1, -1, None, None, FAKE, 0, 32, FAKE, 1 << 40, None) == 2
     r = m.lib.nvfp4_quantize_col16_rht
     assert r(FAKE, 1, 32, 32, 32, 1, -1, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 4     # transform required
     assert r(FAKE, 1, 24, 32, 32, 1, 7, None, FAKE, FAKE, FAKE, FAKE, 4096, None) == 2      # rows % 16
@@ -186,3 +187,28 @@ def test_no_cpu_fallback():
     # every tensor the binding hands to the library must be a device tensor
     with pytest.raises(ValueError):
         m._need_gpu(None, torch.zeros(4))
+
+
+def test_kv_chunked_validation_without_gpu():
+    import nvfp4_w4a4_quantized_04_amd as m
+    q = m.lib.nvfp4_kv_quantize_chunked
+    ws = m.lib.nvfp4_kv_chunked_workspace_size(24, 18480, 128, 7040)
+    assert ws >= 3 * 1024 * 4
+    ok = dict(kv=FAKE, dt=1, h=24, t=100, d=128, tpc=32, rule=1, am=None, c=FAKE, s=FAKE, a=FAKE, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return q(a["kv"], a["dt"], a["h"], a["t"], a["d"], a["tpc"], a["rule"], a["am"], a["c"], a["s"], a["a"],
+                 a["ws"], a["wsb"], None)
+    assert call(dt=7) == 4 and call(rule=2) == 4
+    assert call(d=24) == 2 and call(d=0) == 2 and call(tpc=0) == 2 and call(h=0) == 2 and call(h=1025) == 2
+    assert call(t=1 << 20, tpc=1) == 2                        # more than 65535 chunks
+    assert call(t=0, kv=None) == 0                            # no tokens: nothing to do
+    assert call(kv=None) == 1 and call(a=None) == 1
+    assert call(kv=FAKE + 2) == 3 and call(a=FAKE + 2) == 3
+    assert call(ws=None) == 5 and call(wsb=16) == 5
+    d = m.lib.nvfp4_kv_dequantize_chunked
+    assert d(FAKE, FAKE, FAKE, 24, 100, 128, 32, FAKE, 5, None) == 4
+    assert d(FAKE, FAKE, FAKE, 24, 100, 120, 32, FAKE, 1, None) == 2
+    assert d(FAKE, FAKE, None, 24, 100, 128, 32, FAKE, 1, None) == 1
+    assert d(FAKE, FAKE, FAKE, 24, 100, 128, 32, FAKE + 8, 1, None) == 3

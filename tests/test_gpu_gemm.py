@@ -97,6 +97,40 @@ def test_wgrad_col16():
     assert rel_frobenius(host_bits(dw), ref) <= GEMM_RTOL
 
 
+def test_wgrad_with_handed_amax():
+    """dY's and X's amax handed in (as the forward's GEMM epilogues give them)
+    replace the amax passes: bit-identical dW; an amax that is not the
+    tensor's max is used as given (the oracle quantized with that amax)."""
+    rng = np.random.default_rng(14)
+    t, n, k = 1040, 96, 160
+    x0 = workloads.f32_to_bf16_bits(rng.standard_normal((t, 256)).astype(np.float32))
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((k, 256)) * 0.05).astype(np.float32))
+    dy = workloads.f32_to_bf16_bits((rng.standard_normal((t, n)) * 1e-3).astype(np.float32))
+    print("[case] wgrad handed amax", flush=True)
+    # X is the output of a forward linear; its epilogue amax is max |X|
+    x_amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    xd = nv.linear(dev_from_host(x0), packed_to_device(oracle.quantize(w, oracle.TILE16, 1)), torch.bfloat16,
+                   amax_out=x_amax)
+    dyd = dev_from_host(dy)
+    dy_amax = dyd.float().abs().max().reshape(1)
+    ref = nv.wgrad(dyd, xd, torch.float32)
+    got = nv.wgrad(dyd, xd, torch.float32, dy_amax=dy_amax, x_amax=x_amax)
+    got16 = nv.wgrad(dyd, xd, torch.bfloat16, x_amax=x_amax)
+    torch.cuda.synchronize()
+    assert x_amax.item() == xd.float().abs().max().item()
+    assert np.array_equal(host_bits(got), host_bits(ref))
+    assert np.array_equal(host_bits(got16), oracle.bf16_rne(host_bits(ref)))
+    # a larger amax changes alpha and the codes exactly as the oracle says
+    big = x_amax * 4.0
+    got_big = nv.wgrad(dyd, xd, torch.float32, x_amax=big)
+    torch.cuda.synchronize()
+    xh = host_bits(xd)
+    A = oracle.quantize(dy, oracle.COL16, 1)
+    B = oracle.quantize(xh, oracle.COL16, 1, amax=float(big.item()))
+    assert rel_frobenius(host_bits(got_big), oracle.gemm_f64(A, B)) <= GEMM_RTOL
+    assert not np.array_equal(host_bits(got_big), host_bits(ref))
+
+
 def test_wgrad_col16_rht():
     rng = np.random.default_rng(24)
     t, n, k = 1040, 96, 160
