@@ -714,6 +714,132 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *
     store16(y + (sg.out_row + r) * ldy + cb * 16, val);
 }
 
+// ------------------------------------- KV cache: one global scale per chunk
+
+// The KV cache of heads x tokens key (or value) vectors, [heads][tokens][d],
+// with one global scale per chunk of tokens_per_chunk tokens ("Chunkwise
+// quantization procedure": a per-chunk, per-layer FP32 global scale).  Chunk c
+// holds tokens [c*tpc, min((c+1)*tpc, tokens)) of every head, i.e. `heads`
+// contiguous row segments of the [heads*tokens][d] view.
+struct KvChunks {
+    int64_t tokens, tpc;      // tokens, tokens per chunk
+    int64_t d;                // head_dim
+    int pseg;                 // amax workgroups per (chunk, head) segment
+};
+
+__device__ __forceinline__ int64_t chunk_len(const KvChunks &k, int c)
+{
+    const int64_t t0 = (int64_t)c * k.tpc;
+    return k.tokens - t0 < k.tpc ? k.tokens - t0 : k.tpc;
+}
+
+// Partial maxima: workgroup (p, h, c) reduces part p of the head-h segment of
+// chunk c into partials[c * heads * pseg + h * pseg + p] (same loop shape as
+// k_amax: eight 16-byte loads in flight per thread).
+template <typename T>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__restrict__ x, KvChunks k,
+                                                                  float *__restrict__ partials)
+{
+    __shared__ float red[kAmaxThreads / 64];
+    constexpr int V = 16 / sizeof(T);
+    const int p = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
+    const int64_t len = chunk_len(k, c);
+    const int64_t nv = len * k.d / V;                                   // d % 16 == 0: whole vectors
+    const uint4 *xv = reinterpret_cast<const uint4 *>(x + ((int64_t)h * k.tokens + (int64_t)c * k.tpc) * k.d);
+    const int64_t per_wg = ((nv + k.pseg - 1) / k.pseg + kAmaxThreads - 1) / kAmaxThreads * kAmaxThreads;
+    const int64_t beg = (int64_t)p * per_wg;
+    const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
+    constexpr int64_t kIter = (int64_t)kAmaxThreads * kAmaxUnroll;
+    float a = 0.0f;
+    for (int64_t base = beg; base < end; base += kIter) {
+        uint4 v[kAmaxUnroll];
+#pragma unroll
+        for (int u = 0; u < kAmaxUnroll; u++) {
+            const int64_t i = base + u * kAmaxThreads + threadIdx.x;
+            v[u] = i < end ? xv[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kAmaxUnroll; u++)
+            a = absmax16B<T>(v[u], a);
+    }
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = red[0];
+#pragma unroll
+        for (int w = 1; w < kAmaxThreads / 64; w++)
+            b = fmaxf(b, red[w]);
+        partials[((int64_t)c * gridDim.y + h) * k.pseg + p] = b;
+    }
+}
+
+// Quantize: workgroup (bx, h, c) takes 256 consecutive 16-element blocks of
+// the head-h segment of chunk c, one per lane, with chunk c's alpha (from its
+// n_amax partials at amax_src + c * amax_stride); otherwise as k_quant_row16.
+template <typename T, bool RULE4, int NPT>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__restrict__ x, KvChunks k,
+                                                                    const float *__restrict__ amax_src,
+                                                                    int64_t amax_stride, int n_amax,
+                                                                    uint8_t *__restrict__ codes,
+                                                                    uint8_t *__restrict__ scales,
+                                                                    float *__restrict__ alphas)
+{
+    __shared__ float ktab[128];
+    const int h = blockIdx.y, c = blockIdx.z;
+    const int64_t bpr = k.d / 16;
+    const int64_t nb = chunk_len(k, c) * bpr;                 // blocks of this segment
+    const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads;
+    if (b0 >= nb)
+        return;                                               // the whole workgroup: past a short last chunk
+    const float *src = amax_src + (int64_t)c * amax_stride;
+    const float apart = alpha_issue<NPT>(src, n_amax);
+    const int64_t seg0 = ((int64_t)h * k.tokens + (int64_t)c * k.tpc) * bpr;   // first block of the segment
+    const int64_t bl = b0 + threadIdx.x;
+    const int64_t b = seg0 + (bl < nb ? bl : nb - 1);         // past the end: re-read the last block
+    constexpr int kVec = (int)sizeof(T);
+    uint4 raw[kVec];
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + b * 16);
+#pragma unroll
+    for (int u = 0; u < kVec; u++)
+        raw[u] = p[u];
+    const float alpha = alpha_finish(apart, src, n_amax);
+    build_kappa_table(ktab, alpha);
+    if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0)
+        alphas[c] = alpha;
+    if (bl < nb) {
+        float v[16];
+        unpack16<T>(raw, v);
+        uint32_t c0, c1, sb;
+        quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
+        *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
+        scales[b] = (uint8_t)sb;
+    }
+}
+
+// Dequantize a chunked KV tensor: one lane per 16-element block, alpha of the
+// block's chunk.
+template <typename O>
+__global__ __launch_bounds__(kQuantThreads) void k_dequant_kv_chunked(const uint8_t *__restrict__ codes,
+                                                                      const uint8_t *__restrict__ scales,
+                                                                      const float *__restrict__ alphas, KvChunks k,
+                                                                      int64_t nblocks, O *__restrict__ y)
+{
+    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    if (b >= nblocks)
+        return;
+    const int64_t bpr = k.d / 16;
+    const int64_t row = b / bpr;
+    const int64_t t = row % k.tokens;
+    const uint2 cw = *reinterpret_cast<const uint2 *>(codes + b * 8);
+    const float s = e4m3_get<0>(scales[b]);
+    const float alpha = alphas[t / k.tpc];
+    float v[16];
+    decode16(cw.x, cw.y, s, alpha, v);
+    store16(y + b * 16, v);
+}
+
 // ------------------------------------------------------------ launchers
 
 int amax_partials(int64_t rows, int64_t cols)
@@ -873,6 +999,70 @@ hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, 
         if (rule) k_kv_quant_smoothed<float, true><<<grid, kQuantThreads, 0, s>>>((const float *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
         else      k_kv_quant_smoothed<float, false><<<grid, kQuantThreads, 0, s>>>((const float *)x, vectors, g_log2, means, partials, n, codes, scales, alpha);
     }
+    return hipGetLastError();
+}
+
+int kv_chunk_pseg(int64_t heads, int64_t n_chunks)
+{
+    // about 512 amax workgroups in all, at most kMaxAmaxSrc partials per chunk
+    int64_t p = (512 + heads * n_chunks - 1) / (heads * n_chunks);
+    const int64_t cap = kMaxAmaxSrc / heads;
+    if (p > cap) p = cap;
+    if (p < 1) p = 1;
+    return (int)p;
+}
+
+hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t heads, int64_t tokens, int64_t d,
+                                      int64_t tpc, int rule, const float *chunk_amax, uint8_t *codes,
+                                      uint8_t *scales, float *alphas, float *partials, hipStream_t s)
+{
+    const int64_t nch = (tokens + tpc - 1) / tpc;
+    if (nch == 0)
+        return hipSuccess;
+    KvChunks k{tokens, tpc, d, kv_chunk_pseg(heads, nch)};
+    const float *src = chunk_amax;
+    int64_t stride = 1;
+    int n_amax = 1;
+    if (!chunk_amax) {
+        dim3 ga((unsigned)k.pseg, (unsigned)heads, (unsigned)nch);
+        if (dtype == 1)
+            k_amax_kv_chunked<uint16_t><<<ga, kAmaxThreads, 0, s>>>((const uint16_t *)x, k, partials);
+        else
+            k_amax_kv_chunked<float><<<ga, kAmaxThreads, 0, s>>>((const float *)x, k, partials);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        src = partials;
+        n_amax = (int)(heads * k.pseg);
+        stride = n_amax;
+    }
+    const int64_t bpr = d / 16;
+    const int64_t longest = tpc < tokens ? tpc : tokens;           // tokens of the longest chunk
+    dim3 gq((unsigned)((longest * bpr + kQuantThreads - 1) / kQuantThreads), (unsigned)heads, (unsigned)nch);
+    constexpr int NPT = kMaxAmaxSrc / kQuantThreads;
+    if (dtype == 1) {
+        if (rule) k_quant_kv_chunked<uint16_t, true, NPT><<<gq, kQuantThreads, 0, s>>>((const uint16_t *)x, k, src, stride, n_amax, codes, scales, alphas);
+        else      k_quant_kv_chunked<uint16_t, false, NPT><<<gq, kQuantThreads, 0, s>>>((const uint16_t *)x, k, src, stride, n_amax, codes, scales, alphas);
+    } else {
+        if (rule) k_quant_kv_chunked<float, true, NPT><<<gq, kQuantThreads, 0, s>>>((const float *)x, k, src, stride, n_amax, codes, scales, alphas);
+        else      k_quant_kv_chunked<float, false, NPT><<<gq, kQuantThreads, 0, s>>>((const float *)x, k, src, stride, n_amax, codes, scales, alphas);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
+                                        int64_t heads, int64_t tokens, int64_t d, int64_t tpc, void *y, int ydtype,
+                                        hipStream_t s)
+{
+    const int64_t nblocks = heads * tokens * (d / 16);
+    if (nblocks == 0)
+        return hipSuccess;
+    KvChunks k{tokens, tpc, d, 1};
+    const unsigned grid = (unsigned)((nblocks + kQuantThreads - 1) / kQuantThreads);
+    if (ydtype == 1)
+        k_dequant_kv_chunked<uint16_t><<<grid, kQuantThreads, 0, s>>>(codes, scales, alphas, k, nblocks, (uint16_t *)y);
+    else
+        k_dequant_kv_chunked<float><<<grid, kQuantThreads, 0, s>>>(codes, scales, alphas, k, nblocks, (float *)y);
     return hipGetLastError();
 }
 
