@@ -273,9 +273,25 @@ def bench_kv(nv, workloads, iters):
         kv, p, y, ws, am = sets[i % len(sets)]
         nv.dequantize(p, torch.bfloat16, out=y)
 
+    # the pages' granularity: one global scale per 8-frame chunk (7040 tokens:
+    # chunks of 8, 8 and 5 frames), all chunks in one call
+    tpc = 8 * 880
+    csets = [(nv.kv_quantize_chunked(st[0], tpc),) for st in sets]
+    cws = torch.empty(nv.lib.nvfp4_kv_chunked_workspace_size(heads, tokens, d, tpc), dtype=torch.uint8,
+                      device="cuda")
+    torch.cuda.synchronize()
+
+    def qc(i):
+        nv.kv_quantize_chunked(sets[i % len(sets)][0], tpc, out=csets[i % len(sets)][0], workspace=cws)
+
+    def dqc(i):
+        nv.kv_dequantize_chunked(csets[i % len(sets)][0], torch.bfloat16, out=sets[i % len(sets)][2].view(heads, tokens, d))
+
     t2 = time_events(q2, iters)
     t1 = time_events(q1, iters)
     tdq = time_events(dq, iters)
+    tqc = time_events(qc, iters)
+    tdqc = time_events(dqc, iters)
     bytes_q = n * 2 + n * 9 / 16 + 4          # read bf16, write codes + scales + alpha
     bytes_dq = n * 9 / 16 + 4 + n * 2
 
@@ -284,7 +300,9 @@ def bench_kv(nv, workloads, iters):
         return round(gbps, 1), round(gbps / HBM_PEAK_GBPS, 4)
 
     r2, r1, rd = rate(bytes_q, t2), rate(bytes_q, t1), rate(bytes_dq, tdq)
-    del sets
+    nch = (tokens + tpc - 1) // tpc
+    rc, rdc = rate(bytes_q + 4 * (nch - 1), tqc), rate(bytes_dq + 4 * (nch - 1), tdqc)
+    del sets, csets
     torch.cuda.empty_cache()
     win = bench_kv_window(nv, iters)
     return {
@@ -293,9 +311,16 @@ def bench_kv(nv, workloads, iters):
         "quantize_1pass_ms_per_tensor": round(t1, 5), "quantize_1pass_GBps": r1[0],
         "quantize_1pass_frac_hbm": r1[1],
         "dequantize_ms_per_tensor": round(tdq, 5), "dequantize_GBps": rd[0], "dequantize_frac_hbm": rd[1],
+        "per_chunk_alpha": {
+            "tokens_per_chunk": tpc, "chunks": nch,
+            "quantize_ms_per_tensor": round(tqc, 5), "quantize_GBps": rc[0], "quantize_frac_hbm": rc[1],
+            "dequantize_ms_per_tensor": round(tdqc, 5), "dequantize_GBps": rdc[0], "dequantize_frac_hbm": rdc[1],
+            "note": "one global scale per 8-frame chunk of the 21-frame tensor, all chunks in one call "
+                    "(amax partials per chunk, then the quantizer)"},
         "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
-        "note": "GB/s = algorithmic bytes / event time per call; quantize = amax pass inside the call, "
-                "quantize_1pass = amax supplied by the producing GEMM's epilogue",
+        "note": "GB/s = algorithmic bytes / event time per call, three rotating 113.5 MB tensors; quantize = amax "
+                "pass inside the call (two reads of the tensor), quantize_1pass = amax supplied by the producing "
+                "GEMM's epilogue (one read)",
         "window": win,
     }
 
@@ -314,20 +339,26 @@ def bench_kv_window(nv, iters):
     kc, vc = [], []
     wsz = nv.lib.nvfp4_kv_smooth_workspace_size(rows, d)
     ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    kraw = []
     for c in range(8):
         k = (torch.randn((rows, d), generator=g, device="cuda") + 2.0).to(torch.bfloat16)
         v = torch.randn((rows, d), generator=g, device="cuda").to(torch.bfloat16)
         kc.append(nv.kv_quantize_smoothed(k, workspace=ws))
         vc.append(nv.kv_quantize(v, "4over6"))
+        kraw.append(k)
     torch.cuda.synchronize()
 
+    # the eight raw key chunks in turn (346 MB: no call finds its chunk in the
+    # 256 MB last-level cache)
     def smooth(i):
-        nv.kv_quantize_smoothed(k, out=kc[7][0], means=kc[7][1], workspace=ws)
+        c = i % 8
+        nv.kv_quantize_smoothed(kraw[c], out=kc[c][0], means=kc[c][1], workspace=ws)
 
     t_smooth = time_events(smooth, iters)
     runs = nv.kv_window_plan(64, chunk_frames, 32, 8, 16, 8)
     kparts = [(kc[c][0], kc[c][1], f0 * frame_rows, n * frame_rows) for c, f0, n in runs]
     vparts = [(vc[c], None, f0 * frame_rows, n * frame_rows) for c, f0, n in runs]
+    del kraw
     wrows = sum(p[3] for p in kparts)
     kout = torch.empty((wrows, d), dtype=torch.bfloat16, device="cuda")
     vout = torch.empty((wrows, d), dtype=torch.bfloat16, device="cuda")
@@ -339,15 +370,17 @@ def bench_kv_window(nv, iters):
     t_win = time_events(window, iters)
     n = wrows * d
     bytes_win = 2 * (n * 9 / 16 + n * 2) + wrows * 4          # K and V: packed in, bf16 out; K means
-    bytes_smooth = rows * d * (2 + 2 + 9 / 16) + rows * 4      # two reads of the keys, packed out, means
+    bytes_smooth = rows * d * (2 + 9 / 16) + rows * 4          # keys read once, packed out, means
     gbps = bytes_win / (t_win * 1e-3) / 1e9
     gbs = bytes_smooth / (t_smooth * 1e-3) / 1e9
     return {"workload": f"window of the chunk at frame 64: {len(runs)} chunks x {rows} rows x {d}, K and V",
             "frames": wrows // frame_rows, "window_ms_k_and_v": round(t_win, 5), "window_GBps": round(gbps, 1),
             "window_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "smoothed_k_quantize_ms_per_chunk": round(t_smooth, 5),
             "smoothed_k_quantize_GBps": round(gbs, 1),
-            "note": "window GB/s = (packed K and V + K means read, bf16 K and V written) / time of the two launches; "
-                    "smoothed quantize bytes count both reads of the chunk"}
+            "note": "window GB/s = (packed K and V + K means read, bf16 K and V written) / time of the two launches "
+                    "(518 MB of bf16 output per call between reuses of the packed chunks); smoothed quantize: "
+                    "algorithmic bytes (keys read once, packed keys and means written), eight rotating chunks; the "
+                    "call reads the keys twice (means and amax, then quantize)"}
 
 
 def bench_extra(nv, workloads, iters):
@@ -359,7 +392,11 @@ def bench_extra(nv, workloads, iters):
                             "train_fwd_m32768_k3072_n3072": (32768, 3072, 3072)}.items():
         sets = linear_sets(nv, workloads, m, k, n, 2, 30)
         ms, _ = bench_linear(nv, sets, iters, 3)
-        out[name] = {"ms": round(ms, 4), "TFLOPs": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+        gms = bench_gemm_kernel(nv, sets, iters)
+        tf, gtf = 2 * m * n * k / (ms * 1e-3) / 1e12, 2 * m * n * k / (gms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+                     "gemm_kernel_ms": round(gms, 4), "gemm_kernel_TFLOPs": round(gtf, 1),
+                     "gemm_kernel_frac": round(gtf / FP16_MFMA_PEAK_TFLOPS, 4)}
         del sets
         torch.cuda.empty_cache()
     # the QKV projection with the rank-128 BF16 LoRA branch (alpha 128)
@@ -377,8 +414,9 @@ def bench_extra(nv, workloads, iters):
         nv.linear_lora(x_, w_, la, lb, 1.0, torch.bfloat16, out=y_, workspace=lws, u=u)
 
     ms = time_events(lora_step, iters)
+    tf = 2 * m * (n * k + k * r + n * r) / (ms * 1e-3) / 1e12
     out["qkv_lora_r128_m2640_k3072_n9216"] = {
-        "ms": round(ms, 4), "TFLOPs": round(2 * m * (n * k + k * r + n * r) / (ms * 1e-3) / 1e12, 1),
+        "ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
         "note": "flops of the NVFP4 product plus both LoRA products"}
     del sets
     torch.cuda.empty_cache()
@@ -394,16 +432,42 @@ def bench_extra(nv, workloads, iters):
     def wg(i):
         nv.wgrad(dy, x, torch.bfloat16, out=dw, workspace=ws)
 
+    def entry(ms, note=None):
+        tf = 2 * t * n * k / (ms * 1e-3) / 1e12
+        e = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+        if note:
+            e["note"] = note
+        return e
+
     ms = time_events(wg, iters)
-    out["train_wgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
-                                             "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    out["train_wgrad_t32768_n3072_k3072"] = entry(ms, "amax of dY and X computed inside the call")
+    # the forward already has max |X| (and the producing GEMM of dY its max):
+    # handed in, the two amax passes drop out
+    x_am = x.float().abs().max().reshape(1)
+    dy_am = dy.float().abs().max().reshape(1)
+
+    def wga(i):
+        nv.wgrad(dy, x, torch.bfloat16, out=dw, workspace=ws, dy_amax=dy_am, x_amax=x_am)
+
+    ms = time_events(wga, iters)
+    out["train_wgrad_amax_in_t32768_n3072_k3072"] = entry(
+        ms, "amax of dY and X handed in (the forward's / the producing GEMM's epilogue max), no amax pass")
+    # the GEMM alone on the two COL16-packed operands
+    pa = nv.quantize(dy, "col16", "4over6")
+    pb = nv.quantize(x, "col16", "4over6")
+
+    def wgk(i):
+        nv.gemm(pa, pb, torch.bfloat16, out=dw)
+
+    ms = time_events(wgk, iters)
+    out["train_wgrad_gemm_kernel"] = entry(ms, "the dW GEMM alone on pre-packed operands")
+    del pa, pb
     # the same with the random Hadamard transform on both operands
     def wgr(i):
         nv.wgrad(dy, x, torch.bfloat16, out=dw, workspace=ws, rht_signs=0xC39A)
 
     ms = time_events(wgr, iters)
-    out["train_wgrad_rht_t32768_n3072_k3072"] = {"ms": round(ms, 4),
-                                                 "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    out["train_wgrad_rht_t32768_n3072_k3072"] = entry(ms)
     # data gradient dX = dY W: dY quantized along the 3072 output features, the
     # forward's TILE16 weight transposed once in packed form (not timed)
     w = nv.quantize((torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16), "tile16", "4over6")
@@ -415,8 +479,7 @@ def bench_extra(nv, workloads, iters):
         nv.dgrad(dy, wt, torch.bfloat16, out=dx, workspace=lws)
 
     ms = time_events(dg, iters)
-    out["train_dgrad_t32768_n3072_k3072"] = {"ms": round(ms, 4),
-                                             "TFLOPs": round(2 * t * n * k / (ms * 1e-3) / 1e12, 1)}
+    out["train_dgrad_t32768_n3072_k3072"] = entry(ms)
     del x, dy, dw, ws, w, wt, dx, lws
     torch.cuda.empty_cache()
     # context: the vendor library's dense fp16 / bf16 GEMM (torch.matmul,
@@ -463,6 +526,18 @@ def gpu_outputs_for_parity(nv, workloads):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(workloads, m, k, n, gpu=None):
     """The oracle (fp32 quantizer, fp64 GEMM, OpenMP) on the full QKV step,
     repeated until about 10 s of host time have passed (at most 8 steps).
@@ -482,9 +557,24 @@ def cpu_baseline(workloads, m, k, n, gpu=None):
         steps += 1
     dt = (time.perf_counter() - t0) / steps
     out = {"value": round(2 * m * n * k / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-           "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": steps,
+           "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": steps, "cpu_model": cpu_model(),
            "sample": f"{steps} full QKV steps: amax + four-over-six quantize of X [2640,3072] (fp32 steps) and "
                      "the fp64 GEMM against W [9216,3072] (W quantized once, untimed)"}
+    # the KV round trip on a bounded sample of the KV workload: K of the first
+    # 6 of 24 heads, [6 * 18480, 128], quantized (amax inside) and dequantized
+    kv = workloads.config4()["k"][:6].reshape(-1, 128)
+    t0 = time.perf_counter()
+    R = oracle.quantize(kv, oracle.ROW16, oracle.FOUR_OVER_SIX)
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.dequantize(R)
+    tdq = time.perf_counter() - t0
+    nel = kv.size
+    out["kv_round_trip"] = {
+        "sample": "K of heads 0-5 of the KV workload, [110880, 128] bf16 (a quarter of one tensor)",
+        "quantize_s": round(tq, 3), "quantize_GBps": round(nel * (2 + 9 / 16) / tq / 1e9, 3),
+        "dequantize_s": round(tdq, 3), "dequantize_GBps_fp32_out": round(nel * (9 / 16 + 4) / tdq / 1e9, 3),
+        "note": "algorithmic bytes per second (bf16 in / packed out; packed in / fp32 out), all host cores"}
     if gpu is None:
         return out, None
 
@@ -552,16 +642,20 @@ def main():
         "data": "synthetic (seeded normals shaped like a 5B video DiT's QKV projection)",
         "config": {"workload": "qkv_projection_x2640x3072_w9216x3072_bf16out",
                    "m": m, "k": k, "n": n, "rule": "four-over-six", "weight_blocks": "16x16",
-                   "act_blocks": "1x16", "input_sets": 3, "seeds": [2, 102, 202]},
+                   "act_blocks": "1x16", "input_sets": 4, "seeds": [2, 102, 202, 302],
+                   "rotation_MB": None},
     }
     if "qkv" in parts:
         log("[bench] preparing QKV projection inputs")
-        sets = linear_sets(nv, workloads, m, k, n, 3, 2)
+        sets = linear_sets(nv, workloads, m, k, n, 4, 2)
         log("[bench] timing the fused linear")
         ms, dist = bench_linear(nv, sets, args.steps, args.warmup)
         value = flops / (ms * 1e-3) / 1e12
         log(f"[bench] linear {ms:.4f} ms/step, {value:.1f} TFLOP/s")
         result["step_ms_events"] = dist
+        result["config"]["rotation_MB"] = round(sum(
+            t.numel() * t.element_size() for st in sets for t in (st[0], st[1].codes, st[1].scales, st[2], st[3]))
+            / 1e6, 1)
 
         def step(i):
             x, w, y, ws = sets[i % len(sets)]
