@@ -274,24 +274,27 @@ def bench_kv(nv, workloads, iters):
         nv.dequantize(p, torch.bfloat16, out=y)
 
     # the pages' granularity: one global scale per 8-frame chunk (7040 tokens:
-    # chunks of 8, 8 and 5 frames), all chunks in one call
+    # chunks of 8, 8 and 5 frames) of K and of V, both tensors and all their
+    # chunks in one call; two such [2, heads, tokens, d] pairs alternate
     tpc = 8 * 880
-    csets = [(nv.kv_quantize_chunked(st[0], tpc),) for st in sets]
-    cws = torch.empty(nv.lib.nvfp4_kv_chunked_workspace_size(heads, tokens, d, tpc), dtype=torch.uint8,
+    pairs = [torch.stack((sets[0][0], sets[1][0])), torch.stack((sets[2][0], sets[0][0].neg()))]
+    cpk = [nv.kv_quantize_chunked(p, tpc) for p in pairs]
+    cy = [torch.empty_like(p) for p in pairs]
+    cws = torch.empty(nv.lib.nvfp4_kv_chunked_workspace_size(2, heads, tokens, d, tpc), dtype=torch.uint8,
                       device="cuda")
     torch.cuda.synchronize()
 
     def qc(i):
-        nv.kv_quantize_chunked(sets[i % len(sets)][0], tpc, out=csets[i % len(sets)][0], workspace=cws)
+        nv.kv_quantize_chunked(pairs[i % 2], tpc, out=cpk[i % 2], workspace=cws)
 
     def dqc(i):
-        nv.kv_dequantize_chunked(csets[i % len(sets)][0], torch.bfloat16, out=sets[i % len(sets)][2].view(heads, tokens, d))
+        nv.kv_dequantize_chunked(cpk[i % 2], torch.bfloat16, out=cy[i % 2])
 
     t2 = time_events(q2, iters)
     t1 = time_events(q1, iters)
     tdq = time_events(dq, iters)
-    tqc = time_events(qc, iters)
-    tdqc = time_events(dqc, iters)
+    tqc = time_events(qc, iters) / 2                  # per tensor: each call quantizes K and V
+    tdqc = time_events(dqc, iters) / 2
     bytes_q = n * 2 + n * 9 / 16 + 4          # read bf16, write codes + scales + alpha
     bytes_dq = n * 9 / 16 + 4 + n * 2
 
@@ -302,7 +305,7 @@ def bench_kv(nv, workloads, iters):
     r2, r1, rd = rate(bytes_q, t2), rate(bytes_q, t1), rate(bytes_dq, tdq)
     nch = (tokens + tpc - 1) // tpc
     rc, rdc = rate(bytes_q + 4 * (nch - 1), tqc), rate(bytes_dq + 4 * (nch - 1), tdqc)
-    del sets, csets
+    del sets, pairs, cpk, cy
     torch.cuda.empty_cache()
     win = bench_kv_window(nv, iters)
     return {
@@ -315,8 +318,9 @@ def bench_kv(nv, workloads, iters):
             "tokens_per_chunk": tpc, "chunks": nch,
             "quantize_ms_per_tensor": round(tqc, 5), "quantize_GBps": rc[0], "quantize_frac_hbm": rc[1],
             "dequantize_ms_per_tensor": round(tdqc, 5), "dequantize_GBps": rdc[0], "dequantize_frac_hbm": rdc[1],
-            "note": "one global scale per 8-frame chunk of the 21-frame tensor, all chunks in one call "
-                    "(amax partials per chunk, then the quantizer)"},
+            "note": "one global scale per 8-frame chunk of the 21-frame tensor, K and V and all their chunks "
+                    "in one call (amax partials per tensor and chunk, then the quantizer); time per tensor is "
+                    "half the call"},
         "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
         "note": "GB/s = algorithmic bytes / event time per call, three rotating 113.5 MB tensors; quantize = amax "
                 "pass inside the call (two reads of the tensor), quantize_1pass = amax supplied by the producing "

@@ -336,26 +336,32 @@ nvfp4_status_t nvfp4_transpose_tile16(const uint8_t *codes, const uint8_t *scale
 
 /* ---------------------------------------- KV cache, one scale per chunk */
 
-/* Workspace of nvfp4_kv_quantize_chunked (per-chunk amax partial maxima):
- * 4 KiB per chunk. */
-size_t nvfp4_kv_chunked_workspace_size(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk);
+/* Workspace of nvfp4_kv_quantize_chunked (amax partial maxima): 4 KiB per
+ * (tensor, chunk) unit. */
+size_t nvfp4_kv_chunked_workspace_size(int64_t tensors, int64_t heads, int64_t tokens, int64_t head_dim,
+                                       int64_t tokens_per_chunk);
 
 /*
  * nvfp4_kv_quantize_chunked -- the KV quantizer with one FP32 global scale
- * per CHUNK of tokens, all chunks in one call (two launches: the per-chunk
- * amax partials, then the quantizer; one launch when chunk_amax is given).
- *   kv [heads][tokens][head_dim] (contiguous, 16-byte aligned, fp32 or
- *   bf16); chunk c holds tokens [c * tokens_per_chunk, min((c + 1) *
- *   tokens_per_chunk, tokens)) of every head, n_chunks = ceil(tokens /
- *   tokens_per_chunk).  Each chunk is quantized exactly as nvfp4_kv_quantize
- *   would quantize that chunk alone (16-blocks along head_dim, `rule`).
- *   codes [heads][tokens][head_dim/2], scales [heads][tokens][head_dim/16]:
- *   the ROW16 packing of the [heads * tokens][head_dim] view.
- *   alphas [n_chunks] (fp32, device): chunk c's global scale.
- *   chunk_amax: NULL (computed, one extra read of the tensor) or a device
- *   array [n_chunks] of the chunks' max |x|.
- *   1 <= heads <= 1024, head_dim % 16 == 0 and >= 16, tokens_per_chunk >= 1,
- *   n_chunks <= 65535; tokens == 0 enqueues nothing.
+ * per CHUNK of tokens of each tensor, all chunks (and e.g. a layer's K and V
+ * as two tensors) in one call: two launches, the amax partials of every
+ * (tensor, chunk) unit and then the quantizer; one launch when chunk_amax is
+ * given.
+ *   kv [tensors][heads][tokens][head_dim] (contiguous, 16-byte aligned, fp32
+ *   or bf16); chunk c of tensor u holds tokens [c * tokens_per_chunk,
+ *   min((c + 1) * tokens_per_chunk, tokens)) of every head of u, n_chunks =
+ *   ceil(tokens / tokens_per_chunk).  Each unit is quantized exactly as
+ *   nvfp4_kv_quantize would quantize that chunk of that tensor alone
+ *   (16-blocks along head_dim, `rule`).
+ *   codes [tensors][heads][tokens][head_dim/2], scales
+ *   [tensors][heads][tokens][head_dim/16]: the ROW16 packing of the
+ *   [tensors * heads * tokens][head_dim] view.
+ *   alphas [tensors][n_chunks] (fp32, device): each unit's global scale.
+ *   chunk_amax: NULL (computed, one extra read of the input) or a device
+ *   array [tensors][n_chunks] of the units' max |x|.
+ *   0 <= tensors, 1 <= heads <= 1024, head_dim % 16 == 0 and >= 16,
+ *   tokens_per_chunk >= 1, tensors * n_chunks <= 65535; tensors == 0 or
+ *   tokens == 0 enqueues nothing.
  *   workspace >= nvfp4_kv_chunked_workspace_size() (unused with chunk_amax).
  * Source: "Chunkwise quantization procedure" (a per-chunk, per-layer FP32
  * global scale for the keys and values of each chunk) and "KV cache
@@ -363,22 +369,22 @@ size_t nvfp4_kv_chunked_workspace_size(int64_t heads, int64_t tokens, int64_t he
  * section of the architecture walkthrough page; the paper-notes page gives
  * the chunk size (8 latent frames).
  */
-nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t heads, int64_t tokens,
-                                         int64_t head_dim, int64_t tokens_per_chunk, int rule,
+nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t tensors, int64_t heads,
+                                         int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk, int rule,
                                          const float *chunk_amax, uint8_t *codes, uint8_t *scales,
                                          float *alphas, void *workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
 /*
- * nvfp4_kv_dequantize_chunked -- y = (q * s) * alpha_c for a tensor packed by
- * nvfp4_kv_quantize_chunked with the same (heads, tokens, head_dim,
- * tokens_per_chunk): alpha_c the scale of the element's chunk.  y
- * [heads][tokens][head_dim], contiguous, 16-byte aligned, fp32 or bf16
- * (round to nearest even).
+ * nvfp4_kv_dequantize_chunked -- y = (q * s) * alpha_(u,c) for an input packed
+ * by nvfp4_kv_quantize_chunked with the same (tensors, heads, tokens,
+ * head_dim, tokens_per_chunk): alpha_(u,c) the scale of the element's tensor
+ * and chunk.  y [tensors][heads][tokens][head_dim], contiguous, 16-byte
+ * aligned, fp32 or bf16 (round to nearest even).
  * Source: the "Hierarchical scaling" equation with the per-chunk scale.
  */
 nvfp4_status_t nvfp4_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
-                                           int64_t heads, int64_t tokens, int64_t head_dim,
+                                           int64_t tensors, int64_t heads, int64_t tokens, int64_t head_dim,
                                            int64_t tokens_per_chunk, void *y, int y_dtype, hipStream_t stream);
 
 /* ------------------------------------------------ KV cache, consumer side */

@@ -91,11 +91,11 @@ def _load():
     L.nvfp4_transpose_tile16.restype = i32
     L.nvfp4_transpose_tile16.argtypes = [P, P, P, i64, i64, P, P, P, P]
     L.nvfp4_kv_chunked_workspace_size.restype = sz
-    L.nvfp4_kv_chunked_workspace_size.argtypes = [i64, i64, i64, i64]
+    L.nvfp4_kv_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     L.nvfp4_kv_quantize_chunked.restype = i32
-    L.nvfp4_kv_quantize_chunked.argtypes = [P, i32, i64, i64, i64, i64, i32, P, P, P, P, P, sz, P]
+    L.nvfp4_kv_quantize_chunked.argtypes = [P, i32, i64, i64, i64, i64, i64, i32, P, P, P, P, P, sz, P]
     L.nvfp4_kv_dequantize_chunked.restype = i32
-    L.nvfp4_kv_dequantize_chunked.argtypes = [P, P, P, i64, i64, i64, i64, P, i32, P]
+    L.nvfp4_kv_dequantize_chunked.argtypes = [P, P, P, i64, i64, i64, i64, i64, P, i32, P]
     L.nvfp4_linear_no_alloc.restype = i32
     L.nvfp4_linear_no_alloc.argtypes = [P, i32, i64, i64, i64, i32, P, P, P, i32, i64, P, i32, i64, P, P]
     return L
@@ -451,61 +451,74 @@ def quantize_col16_rht(x: torch.Tensor, signs: int, rule="4over6", amax: torch.T
 
 
 class KvChunked:
-    """A KV tensor [heads][tokens][head_dim] packed with one global scale per
-    chunk of tokens: codes [heads, tokens, d/2], scales [heads, tokens, d/16]
-    (uint8), alphas [n_chunks] (float32)."""
+    """KV tensors [*lead, heads, tokens, head_dim] (lead = () for one tensor,
+    (tensors,) for several, e.g. a layer's K and V) packed with one global
+    scale per tensor and chunk of tokens: codes [*lead, heads, tokens, d/2],
+    scales [*lead, heads, tokens, d/16] (uint8), alphas [*lead, n_chunks]
+    (float32)."""
 
-    def __init__(self, codes, scales, alphas, heads, tokens, head_dim, tokens_per_chunk):
+    def __init__(self, codes, scales, alphas, heads, tokens, head_dim, tokens_per_chunk, lead=()):
         self.codes, self.scales, self.alphas = codes, scales, alphas
         self.heads, self.tokens, self.head_dim, self.tokens_per_chunk = heads, tokens, head_dim, tokens_per_chunk
+        self.lead = tuple(lead)
+
+    @property
+    def tensors(self) -> int:
+        return self.lead[0] if self.lead else 1
 
 
 def kv_quantize_chunked(kv: torch.Tensor, tokens_per_chunk: int, rule="4over6",
                         out: KvChunked | None = None, chunk_amax: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None) -> KvChunked:
     """quantize_kv with the pages' per-chunk global scale: kv [heads, tokens,
-    head_dim] contiguous; chunk c = tokens [c*tpc, (c+1)*tpc) of every head.
-    chunk_amax (float32 [n_chunks], optional): the chunks' max |x|."""
+    head_dim] or [tensors, heads, tokens, head_dim] contiguous; chunk c of a
+    tensor = tokens [c*tpc, (c+1)*tpc) of its every head.  chunk_amax
+    (float32 [tensors * n_chunks], optional): the units' max |x|."""
     _need_gpu(kv)
-    if kv.dim() != 3 or not kv.is_contiguous():
-        raise ValueError("kv must be a contiguous [heads, tokens, head_dim] tensor")
-    heads, tokens, d = kv.shape
+    if kv.dim() not in (3, 4) or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [(tensors,) heads, tokens, head_dim] tensor")
+    lead = tuple(kv.shape[:-3])
+    tensors = lead[0] if lead else 1
+    heads, tokens, d = kv.shape[-3:]
     tpc = int(tokens_per_chunk)
     nch = (tokens + tpc - 1) // tpc if tpc > 0 else 0
     if out is None:
         dev = kv.device
-        out = KvChunked(torch.empty((heads, tokens, d // 2), dtype=torch.uint8, device=dev),
-                        torch.empty((heads, tokens, d // 16), dtype=torch.uint8, device=dev),
-                        torch.empty(max(nch, 1), dtype=torch.float32, device=dev), heads, tokens, d, tpc)
-    if out.codes.shape != (heads, tokens, d // 2) or out.scales.shape != (heads, tokens, d // 16):
+        out = KvChunked(torch.empty(lead + (heads, tokens, d // 2), dtype=torch.uint8, device=dev),
+                        torch.empty(lead + (heads, tokens, d // 16), dtype=torch.uint8, device=dev),
+                        torch.empty(lead + (max(nch, 1),), dtype=torch.float32, device=dev),
+                        heads, tokens, d, tpc, lead)
+    if (tuple(out.codes.shape) != lead + (heads, tokens, d // 2) or
+            tuple(out.scales.shape) != lead + (heads, tokens, d // 16)):
         raise ValueError("output packed tensor has the wrong shape")
     for t, what in ((out.codes, "codes"), (out.scales, "scales")):
         if t.dtype != torch.uint8 or not t.is_contiguous():
             raise ValueError(f"{what} must be contiguous uint8")
-    _check_vec(out.alphas, nch, torch.float32, "alphas")
-    _check_vec(chunk_amax, nch, torch.float32, "chunk_amax")
+    _check_vec(out.alphas, tensors * nch, torch.float32, "alphas")
+    _check_vec(chunk_amax, tensors * nch, torch.float32, "chunk_amax")
     if workspace is None:
-        workspace = torch.empty(lib.nvfp4_kv_chunked_workspace_size(heads, tokens, d, tpc), dtype=torch.uint8,
-                                device=kv.device)
+        workspace = torch.empty(lib.nvfp4_kv_chunked_workspace_size(tensors, heads, tokens, d, tpc),
+                                dtype=torch.uint8, device=kv.device)
     _need_gpu(out.codes, out.scales, out.alphas, chunk_amax, workspace)
     _check("nvfp4_kv_quantize_chunked", lib.nvfp4_kv_quantize_chunked(
-        _ptr(kv), _dtype_code(kv), heads, tokens, d, tpc, _rule(rule), _ptr(chunk_amax), _ptr(out.codes),
-        _ptr(out.scales), _ptr(out.alphas), _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(kv), _dtype_code(kv), tensors, heads, tokens, d, tpc, _rule(rule), _ptr(chunk_amax),
+        _ptr(out.codes), _ptr(out.scales), _ptr(out.alphas), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
 def kv_dequantize_chunked(t: KvChunked, dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
-    """(q * s) * alpha of each element's chunk, [heads, tokens, head_dim]."""
+    """(q * s) * alpha of each element's tensor and chunk, [*lead, heads,
+    tokens, head_dim]."""
     _need_gpu(t.codes, t.scales, t.alphas)
-    shape = (t.heads, t.tokens, t.head_dim)
+    shape = t.lead + (t.heads, t.tokens, t.head_dim)
     if out is None:
         out = torch.empty(shape, dtype=dtype, device=t.codes.device)
     if tuple(out.shape) != shape or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [heads, tokens, head_dim] tensor")
+        raise ValueError("out must be a contiguous tensor of the packed tensor's shape")
     _need_gpu(out)
     _check("nvfp4_kv_dequantize_chunked", lib.nvfp4_kv_dequantize_chunked(
-        _ptr(t.codes), _ptr(t.scales), _ptr(t.alphas), t.heads, t.tokens, t.head_dim, t.tokens_per_chunk,
-        _ptr(out), _out_dtype_code(out.dtype), _stream()))
+        _ptr(t.codes), _ptr(t.scales), _ptr(t.alphas), t.tensors, t.heads, t.tokens, t.head_dim,
+        t.tokens_per_chunk, _ptr(out), _out_dtype_code(out.dtype), _stream()))
     return out
 
 

@@ -497,42 +497,46 @@ nvfp4_status_t nvfp4_quantize_col16_rht(const void *x, int x_dtype, int64_t rows
                        (float *)workspace, stream, rht_signs);
 }
 
-size_t nvfp4_kv_chunked_workspace_size(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk)
+size_t nvfp4_kv_chunked_workspace_size(int64_t tensors, int64_t heads, int64_t tokens, int64_t head_dim,
+                                       int64_t tokens_per_chunk)
 {
     (void)heads; (void)head_dim;
-    if (tokens <= 0 || tokens_per_chunk <= 0)
+    if (tensors <= 0 || tokens <= 0 || tokens_per_chunk <= 0)
         return kAlignWs;
     const int64_t nch = (tokens + tokens_per_chunk - 1) / tokens_per_chunk;
-    return round_up((size_t)nch * kMaxAmaxSrc * sizeof(float), kAlignWs);
+    return round_up((size_t)tensors * (size_t)nch * kMaxAmaxSrc * sizeof(float), kAlignWs);
 }
 
 namespace {
 // The checks shared by the chunked KV quantize and dequantize.
-nvfp4_status_t check_kv_chunked(int64_t heads, int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk)
+nvfp4_status_t check_kv_chunked(int64_t tensors, int64_t heads, int64_t tokens, int64_t head_dim,
+                                int64_t tokens_per_chunk)
 {
-    if (heads < 1 || heads > kMaxAmaxSrc || tokens < 0 || head_dim < 16 || head_dim % 16 != 0 ||
-        tokens_per_chunk < 1 || tokens >= kMaxDim || head_dim >= kMaxDim || !lanes_fit(heads * tokens, head_dim))
+    if (tensors < 0 || tensors > 65535 || heads < 1 || heads > kMaxAmaxSrc || tokens < 0 || head_dim < 16 ||
+        head_dim % 16 != 0 || tokens_per_chunk < 1 || tokens >= kMaxDim || head_dim >= kMaxDim ||
+        !lanes_fit(tensors * heads * tokens, head_dim))
         return NVFP4_ERR_SHAPE;
     const int64_t nch = (tokens + tokens_per_chunk - 1) / tokens_per_chunk;
     const int64_t bpr = head_dim / 16;
-    // grid limits of the launches: chunks and quantize workgroups per segment
-    if (nch > 65535 || (tokens_per_chunk < tokens ? tokens_per_chunk : tokens) * bpr / kQuantThreads >= 0x7fffffff)
+    // grid limits of the launches: units (tensor, chunk) and quantize workgroups per segment
+    if (tensors * nch > 65535 ||
+        (tokens_per_chunk < tokens ? tokens_per_chunk : tokens) * bpr / kQuantThreads >= 0x7fffffff)
         return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
 }
 }  // namespace
 
-nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t heads, int64_t tokens,
-                                         int64_t head_dim, int64_t tokens_per_chunk, int rule,
+nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t tensors, int64_t heads,
+                                         int64_t tokens, int64_t head_dim, int64_t tokens_per_chunk, int rule,
                                          const float *chunk_amax, uint8_t *codes, uint8_t *scales, float *alphas,
                                          void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!dtype_ok(kv_dtype) || !rule_ok(rule))
         return NVFP4_ERR_DTYPE;
-    nvfp4_status_t st = check_kv_chunked(heads, tokens, head_dim, tokens_per_chunk);
+    nvfp4_status_t st = check_kv_chunked(tensors, heads, tokens, head_dim, tokens_per_chunk);
     if (st != NVFP4_OK)
         return st;
-    if (tokens == 0)
+    if (tokens == 0 || tensors == 0)
         return NVFP4_OK;                                  // no chunk, nothing to write
     if (!kv || !codes || !scales || !alphas)
         return NVFP4_ERR_NULL;
@@ -540,33 +544,33 @@ nvfp4_status_t nvfp4_kv_quantize_chunked(const void *kv, int kv_dtype, int64_t h
         ((uintptr_t)chunk_amax & 3u))
         return NVFP4_ERR_ALIGN;
     if (!chunk_amax) {
-        if (!workspace || workspace_bytes < nvfp4_kv_chunked_workspace_size(heads, tokens, head_dim,
+        if (!workspace || workspace_bytes < nvfp4_kv_chunked_workspace_size(tensors, heads, tokens, head_dim,
                                                                             tokens_per_chunk))
             return NVFP4_ERR_WORKSPACE;
         if (!aligned16(workspace))
             return NVFP4_ERR_ALIGN;
     }
-    return launch_status(launch_kv_quantize_chunked(kv, kv_dtype, heads, tokens, head_dim, tokens_per_chunk, rule,
-                                                    chunk_amax, codes, scales, alphas, (float *)workspace,
-                                                    stream));
+    return launch_status(launch_kv_quantize_chunked(kv, kv_dtype, tensors, heads, tokens, head_dim,
+                                                    tokens_per_chunk, rule, chunk_amax, codes, scales, alphas,
+                                                    (float *)workspace, stream));
 }
 
 nvfp4_status_t nvfp4_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
-                                           int64_t heads, int64_t tokens, int64_t head_dim,
+                                           int64_t tensors, int64_t heads, int64_t tokens, int64_t head_dim,
                                            int64_t tokens_per_chunk, void *y, int y_dtype, hipStream_t stream)
 {
     if (!dtype_ok(y_dtype))
         return NVFP4_ERR_DTYPE;
-    nvfp4_status_t st = check_kv_chunked(heads, tokens, head_dim, tokens_per_chunk);
+    nvfp4_status_t st = check_kv_chunked(tensors, heads, tokens, head_dim, tokens_per_chunk);
     if (st != NVFP4_OK)
         return st;
-    if (tokens == 0)
+    if (tokens == 0 || tensors == 0)
         return NVFP4_OK;
     if (!codes || !scales || !alphas || !y)
         return NVFP4_ERR_NULL;
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(y) || ((uintptr_t)alphas & 3u))
         return NVFP4_ERR_ALIGN;
-    return launch_status(launch_kv_dequantize_chunked(codes, scales, alphas, heads, tokens, head_dim,
+    return launch_status(launch_kv_dequantize_chunked(codes, scales, alphas, tensors, heads, tokens, head_dim,
                                                       tokens_per_chunk, y, y_dtype, stream));
 }
 

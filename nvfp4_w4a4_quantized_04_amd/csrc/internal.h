@@ -42,17 +42,18 @@ hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, 
                                      uint8_t *codes, uint8_t *scales, float *alpha, float *means, float *partials,
                                      hipStream_t s);
 
-// KV cache [heads][tokens][d] with one alpha per chunk of tpc tokens:
-// per-chunk amax partials (unless chunk_amax [n_chunks] is given), then the
-// ROW16 quantizer with each chunk's alpha; alphas [n_chunks].  partials:
-// n_chunks * kMaxAmaxSrc floats of scratch.  heads <= kMaxAmaxSrc.
-int kv_chunk_pseg(int64_t heads, int64_t n_chunks);
-hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t heads, int64_t tokens, int64_t d,
-                                      int64_t tpc, int rule, const float *chunk_amax, uint8_t *codes,
+// KV caches [tensors][heads][tokens][d] with one alpha per tensor and chunk of
+// tpc tokens: per-unit amax partials (unless chunk_amax [tensors][n_chunks]
+// is given), then the ROW16 quantizer with each unit's alpha; alphas
+// [tensors][n_chunks].  partials: tensors * n_chunks * kMaxAmaxSrc floats of
+// scratch.  heads <= kMaxAmaxSrc.
+int kv_chunk_pseg(int64_t heads, int64_t units);
+hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t tensors, int64_t heads, int64_t tokens,
+                                      int64_t d, int64_t tpc, int rule, const float *chunk_amax, uint8_t *codes,
                                       uint8_t *scales, float *alphas, float *partials, hipStream_t s);
 hipError_t launch_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
-                                        int64_t heads, int64_t tokens, int64_t d, int64_t tpc, void *y, int ydtype,
-                                        hipStream_t s);
+                                        int64_t tensors, int64_t heads, int64_t tokens, int64_t d, int64_t tpc,
+                                        void *y, int ydtype, hipStream_t s);
 
 // Window reconstruction from cached chunks (segment table passed by value).
 constexpr int kMaxKvSegments = 32;

@@ -79,11 +79,11 @@ __device__ __forceinline__ float absmax16B(uint4 v, float a)
 // last iteration's loads are predicated, not serialized).
 template <typename T>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
-                                                       int64_t ldx, float *__restrict__ partials)
+                                                       int64_t ldx, bool vec, float *__restrict__ partials)
 {
     __shared__ float red[kAmaxThreads / 64];
     float a = 0.0f;
-    if (ldx == cols) {
+    if (vec) {                                  // contiguous and 16-byte aligned: flat 16-byte loads
         constexpr int V = 16 / sizeof(T);
         const int64_t n = rows * cols;
         const int64_t nv = n / V;
@@ -716,25 +716,36 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *
 
 // ------------------------------------- KV cache: one global scale per chunk
 
-// The KV cache of heads x tokens key (or value) vectors, [heads][tokens][d],
-// with one global scale per chunk of tokens_per_chunk tokens ("Chunkwise
-// quantization procedure": a per-chunk, per-layer FP32 global scale).  Chunk c
-// holds tokens [c*tpc, min((c+1)*tpc, tokens)) of every head, i.e. `heads`
-// contiguous row segments of the [heads*tokens][d] view.
+// KV caches of heads x tokens key (or value) vectors, [tensors][heads][tokens][d]
+// (e.g. K and V of a layer as two tensors), with one global scale per tensor
+// and chunk of tokens_per_chunk tokens ("Chunkwise quantization procedure": a
+// per-chunk, per-layer FP32 global scale).  Chunk c of tensor u holds tokens
+// [c*tpc, min((c+1)*tpc, tokens)) of every head of u, i.e. `heads` contiguous
+// row segments of the [tensors*heads*tokens][d] view.  Unit z = u * nch + c
+// (grid z) indexes the scales, the amax partials and chunk_amax.
 struct KvChunks {
     int64_t tokens, tpc;      // tokens, tokens per chunk
     int64_t d;                // head_dim
-    int pseg;                 // amax workgroups per (chunk, head) segment
+    int64_t heads;
+    int nch;                  // chunks per tensor
+    int pseg;                 // amax workgroups per (unit, head) segment
 };
 
-__device__ __forceinline__ int64_t chunk_len(const KvChunks &k, int c)
+// first row of the head-h segment of unit z
+__device__ __forceinline__ int64_t unit_row0(const KvChunks &k, int z, int h)
 {
-    const int64_t t0 = (int64_t)c * k.tpc;
+    const int u = z / k.nch, c = z - u * k.nch;
+    return ((int64_t)u * k.heads + h) * k.tokens + (int64_t)c * k.tpc;
+}
+
+__device__ __forceinline__ int64_t chunk_len(const KvChunks &k, int z)
+{
+    const int64_t t0 = (int64_t)(z % k.nch) * k.tpc;
     return k.tokens - t0 < k.tpc ? k.tokens - t0 : k.tpc;
 }
 
-// Partial maxima: workgroup (p, h, c) reduces part p of the head-h segment of
-// chunk c into partials[c * heads * pseg + h * pseg + p] (same loop shape as
+// Partial maxima: workgroup (p, h, z) reduces part p of the head-h segment of
+// unit z into partials[z * heads * pseg + h * pseg + p] (same loop shape as
 // k_amax: eight 16-byte loads in flight per thread).
 template <typename T>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__restrict__ x, KvChunks k,
@@ -742,10 +753,10 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__res
 {
     __shared__ float red[kAmaxThreads / 64];
     constexpr int V = 16 / sizeof(T);
-    const int p = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-    const int64_t len = chunk_len(k, c);
+    const int p = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+    const int64_t len = chunk_len(k, z);
     const int64_t nv = len * k.d / V;                                   // d % 16 == 0: whole vectors
-    const uint4 *xv = reinterpret_cast<const uint4 *>(x + ((int64_t)h * k.tokens + (int64_t)c * k.tpc) * k.d);
+    const uint4 *xv = reinterpret_cast<const uint4 *>(x + unit_row0(k, z, h) * k.d);
     const int64_t per_wg = ((nv + k.pseg - 1) / k.pseg + kAmaxThreads - 1) / kAmaxThreads * kAmaxThreads;
     const int64_t beg = (int64_t)p * per_wg;
     const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
@@ -771,13 +782,13 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__res
 #pragma unroll
         for (int w = 1; w < kAmaxThreads / 64; w++)
             b = fmaxf(b, red[w]);
-        partials[((int64_t)c * gridDim.y + h) * k.pseg + p] = b;
+        partials[((int64_t)z * gridDim.y + h) * k.pseg + p] = b;
     }
 }
 
-// Quantize: workgroup (bx, h, c) takes 256 consecutive 16-element blocks of
-// the head-h segment of chunk c, one per lane, with chunk c's alpha (from its
-// n_amax partials at amax_src + c * amax_stride); otherwise as k_quant_row16.
+// Quantize: workgroup (bx, h, z) takes 256 consecutive 16-element blocks of
+// the head-h segment of unit z, one per lane, with unit z's alpha (from its
+// n_amax partials at amax_src + z * amax_stride); otherwise as k_quant_row16.
 template <typename T, bool RULE4, int NPT>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__restrict__ x, KvChunks k,
                                                                     const float *__restrict__ amax_src,
@@ -787,15 +798,15 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__r
                                                                     float *__restrict__ alphas)
 {
     __shared__ float ktab[128];
-    const int h = blockIdx.y, c = blockIdx.z;
+    const int h = blockIdx.y, z = blockIdx.z;
     const int64_t bpr = k.d / 16;
-    const int64_t nb = chunk_len(k, c) * bpr;                 // blocks of this segment
+    const int64_t nb = chunk_len(k, z) * bpr;                 // blocks of this segment
     const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads;
     if (b0 >= nb)
         return;                                               // the whole workgroup: past a short last chunk
-    const float *src = amax_src + (int64_t)c * amax_stride;
+    const float *src = amax_src + (int64_t)z * amax_stride;
     const float apart = alpha_issue<NPT>(src, n_amax);
-    const int64_t seg0 = ((int64_t)h * k.tokens + (int64_t)c * k.tpc) * bpr;   // first block of the segment
+    const int64_t seg0 = unit_row0(k, z, h) * bpr;            // first block of the segment
     const int64_t bl = b0 + threadIdx.x;
     const int64_t b = seg0 + (bl < nb ? bl : nb - 1);         // past the end: re-read the last block
     constexpr int kVec = (int)sizeof(T);
@@ -807,7 +818,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__r
     const float alpha = alpha_finish(apart, src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0)
-        alphas[c] = alpha;
+        alphas[z] = alpha;
     if (bl < nb) {
         float v[16];
         unpack16<T>(raw, v);
@@ -831,10 +842,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_kv_chunked(const uint
         return;
     const int64_t bpr = k.d / 16;
     const int64_t row = b / bpr;
-    const int64_t t = row % k.tokens;
+    const int64_t ht = row / k.tokens;                        // tensor * heads + head
+    const int64_t t = row - ht * k.tokens;
     const uint2 cw = *reinterpret_cast<const uint2 *>(codes + b * 8);
     const float s = e4m3_get<0>(scales[b]);
-    const float alpha = alphas[t / k.tpc];
+    const float alpha = alphas[(ht / k.heads) * k.nch + t / k.tpc];
     float v[16];
     decode16(cw.x, cw.y, s, alpha, v);
     store16(y + b * 16, v);
@@ -857,10 +869,13 @@ int amax_partials(int64_t rows, int64_t cols)
 hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
                        int n_partials, hipStream_t s)
 {
+    // the flat vector path needs whole 16-byte vectors: entry points that take
+    // element-aligned inputs (COL16, WGRAD) fall back to the row loop
+    const bool vec = ldx == cols && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
     if (dtype == 1)
-        k_amax<uint16_t><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, partials);
+        k_amax<uint16_t><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, vec, partials);
     else
-        k_amax<float><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, partials);
+        k_amax<float><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, vec, partials);
     return hipGetLastError();
 }
 
@@ -1002,29 +1017,30 @@ hipError_t launch_kv_smooth_quantize(const void *x, int dtype, int64_t vectors, 
     return hipGetLastError();
 }
 
-int kv_chunk_pseg(int64_t heads, int64_t n_chunks)
+int kv_chunk_pseg(int64_t heads, int64_t units)
 {
-    // about 512 amax workgroups in all, at most kMaxAmaxSrc partials per chunk
-    int64_t p = (512 + heads * n_chunks - 1) / (heads * n_chunks);
+    // about 512 amax workgroups in all, at most kMaxAmaxSrc partials per unit
+    int64_t p = (512 + heads * units - 1) / (heads * units);
     const int64_t cap = kMaxAmaxSrc / heads;
     if (p > cap) p = cap;
     if (p < 1) p = 1;
     return (int)p;
 }
 
-hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t heads, int64_t tokens, int64_t d,
-                                      int64_t tpc, int rule, const float *chunk_amax, uint8_t *codes,
+hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t tensors, int64_t heads, int64_t tokens,
+                                      int64_t d, int64_t tpc, int rule, const float *chunk_amax, uint8_t *codes,
                                       uint8_t *scales, float *alphas, float *partials, hipStream_t s)
 {
     const int64_t nch = (tokens + tpc - 1) / tpc;
-    if (nch == 0)
+    if (nch == 0 || tensors == 0)
         return hipSuccess;
-    KvChunks k{tokens, tpc, d, kv_chunk_pseg(heads, nch)};
+    const int64_t units = tensors * nch;
+    KvChunks k{tokens, tpc, d, heads, (int)nch, kv_chunk_pseg(heads, units)};
     const float *src = chunk_amax;
     int64_t stride = 1;
     int n_amax = 1;
     if (!chunk_amax) {
-        dim3 ga((unsigned)k.pseg, (unsigned)heads, (unsigned)nch);
+        dim3 ga((unsigned)k.pseg, (unsigned)heads, (unsigned)units);
         if (dtype == 1)
             k_amax_kv_chunked<uint16_t><<<ga, kAmaxThreads, 0, s>>>((const uint16_t *)x, k, partials);
         else
@@ -1038,7 +1054,7 @@ hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t heads, i
     }
     const int64_t bpr = d / 16;
     const int64_t longest = tpc < tokens ? tpc : tokens;           // tokens of the longest chunk
-    dim3 gq((unsigned)((longest * bpr + kQuantThreads - 1) / kQuantThreads), (unsigned)heads, (unsigned)nch);
+    dim3 gq((unsigned)((longest * bpr + kQuantThreads - 1) / kQuantThreads), (unsigned)heads, (unsigned)units);
     constexpr int NPT = kMaxAmaxSrc / kQuantThreads;
     if (dtype == 1) {
         if (rule) k_quant_kv_chunked<uint16_t, true, NPT><<<gq, kQuantThreads, 0, s>>>((const uint16_t *)x, k, src, stride, n_amax, codes, scales, alphas);
@@ -1051,13 +1067,13 @@ hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t heads, i
 }
 
 hipError_t launch_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *scales, const float *alphas,
-                                        int64_t heads, int64_t tokens, int64_t d, int64_t tpc, void *y, int ydtype,
-                                        hipStream_t s)
+                                        int64_t tensors, int64_t heads, int64_t tokens, int64_t d, int64_t tpc,
+                                        void *y, int ydtype, hipStream_t s)
 {
-    const int64_t nblocks = heads * tokens * (d / 16);
+    const int64_t nblocks = tensors * heads * tokens * (d / 16);
     if (nblocks == 0)
         return hipSuccess;
-    KvChunks k{tokens, tpc, d, 1};
+    KvChunks k{tokens, tpc, d, heads, (int)((tokens + tpc - 1) / tpc), 1};
     const unsigned grid = (unsigned)((nblocks + kQuantThreads - 1) / kQuantThreads);
     if (ydtype == 1)
         k_dequant_kv_chunked<uint16_t><<<grid, kQuantThreads, 0, s>>>(codes, scales, alphas, k, nblocks, (uint16_t *)y);

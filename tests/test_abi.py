@@ -192,23 +192,28 @@ def test_no_cpu_fallback():
 def test_kv_chunked_validation_without_gpu():
     import nvfp4_w4a4_quantized_04_amd as m
     q = m.lib.nvfp4_kv_quantize_chunked
-    ws = m.lib.nvfp4_kv_chunked_workspace_size(24, 18480, 128, 7040)
+    ws = m.lib.nvfp4_kv_chunked_workspace_size(1, 24, 18480, 128, 7040)
     assert ws >= 3 * 1024 * 4
-    ok = dict(kv=FAKE, dt=1, h=24, t=100, d=128, tpc=32, rule=1, am=None, c=FAKE, s=FAKE, a=FAKE, ws=FAKE, wsb=1 << 20)
+    assert m.lib.nvfp4_kv_chunked_workspace_size(2, 24, 18480, 128, 7040) >= 2 * 3 * 1024 * 4
+    ok = dict(kv=FAKE, dt=1, n=2, h=24, t=100, d=128, tpc=32, rule=1, am=None, c=FAKE, s=FAKE, a=FAKE, ws=FAKE,
+              wsb=1 << 20)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return q(a["kv"], a["dt"], a["h"], a["t"], a["d"], a["tpc"], a["rule"], a["am"], a["c"], a["s"], a["a"],
-                 a["ws"], a["wsb"], None)
+        return q(a["kv"], a["dt"], a["n"], a["h"], a["t"], a["d"], a["tpc"], a["rule"], a["am"], a["c"], a["s"],
+                 a["a"], a["ws"], a["wsb"], None)
     assert call(dt=7) == 4 and call(rule=2) == 4
     assert call(d=24) == 2 and call(d=0) == 2 and call(tpc=0) == 2 and call(h=0) == 2 and call(h=1025) == 2
+    assert call(n=-1) == 2
     assert call(t=1 << 20, tpc=1) == 2                        # more than 65535 chunks
+    assert call(t=40000, tpc=1) == 2                          # 2 tensors x 40000 chunks: more than 65535 units
     assert call(t=0, kv=None) == 0                            # no tokens: nothing to do
+    assert call(n=0, kv=None) == 0                            # no tensors: nothing to do
     assert call(kv=None) == 1 and call(a=None) == 1
     assert call(kv=FAKE + 2) == 3 and call(a=FAKE + 2) == 3
     assert call(ws=None) == 5 and call(wsb=16) == 5
     d = m.lib.nvfp4_kv_dequantize_chunked
-    assert d(FAKE, FAKE, FAKE, 24, 100, 128, 32, FAKE, 5, None) == 4
-    assert d(FAKE, FAKE, FAKE, 24, 100, 120, 32, FAKE, 1, None) == 2
-    assert d(FAKE, FAKE, None, 24, 100, 128, 32, FAKE, 1, None) == 1
-    assert d(FAKE, FAKE, FAKE, 24, 100, 128, 32, FAKE + 8, 1, None) == 3
+    assert d(FAKE, FAKE, FAKE, 2, 24, 100, 128, 32, FAKE, 5, None) == 4
+    assert d(FAKE, FAKE, FAKE, 2, 24, 100, 120, 32, FAKE, 1, None) == 2
+    assert d(FAKE, FAKE, None, 2, 24, 100, 128, 32, FAKE, 1, None) == 1
+    assert d(FAKE, FAKE, FAKE, 2, 24, 100, 128, 32, FAKE + 8, 1, None) == 3

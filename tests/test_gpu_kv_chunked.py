@@ -27,15 +27,19 @@ def _oracle_chunks(kv, tpc, rule):
 
 
 def _check(kv, tpc, rule, chunk_amax=False):
-    heads, tokens, d = kv.shape
-    print(f"[case] kv chunked heads={heads} tokens={tokens} d={d} tpc={tpc} rule={rule} dtype={kv.dtype} "
-          f"amax_in={chunk_amax}", flush=True)
-    refs = _oracle_chunks(kv, tpc, rule)
+    """kv [heads, tokens, d] (one tensor) or [tensors, heads, tokens, d]: every
+    (tensor, chunk) unit against the oracle run on that chunk of that tensor."""
+    heads, tokens, d = kv.shape[-3:]
+    many = kv.ndim == 4
+    print(f"[case] kv chunked shape={kv.shape} tpc={tpc} rule={rule} dtype={kv.dtype} amax_in={chunk_amax}",
+          flush=True)
+    per = [_oracle_chunks(t, tpc, rule) for t in (kv if many else kv[None])]
     kd = dev_from_host(kv)
     am = None
     if chunk_amax:
-        am = torch.tensor([float(oracle.amax(np.ascontiguousarray(kv[:, t0:t1, :]).reshape(-1, d)))
-                           for t0, t1, _ in refs], dtype=torch.float32).cuda()
+        am = torch.tensor([float(oracle.amax(np.ascontiguousarray(t[:, t0:t1, :]).reshape(-1, d)))
+                           for t, refs in zip(kv if many else kv[None], per) for t0, t1, _ in refs],
+                          dtype=torch.float32).cuda()
     got = nv.kv_quantize_chunked(kd, tpc, rule, chunk_amax=am)
     y32 = nv.kv_dequantize_chunked(got, torch.float32)
     y16 = nv.kv_dequantize_chunked(got, torch.bfloat16)
@@ -43,13 +47,17 @@ def _check(kv, tpc, rule, chunk_amax=False):
     codes, scales = got.codes.cpu().numpy(), got.scales.cpu().numpy()
     alphas = got.alphas.cpu().numpy()
     g32, g16 = host_bits(y32), host_bits(y16)
-    for c, (t0, t1, R) in enumerate(refs):
-        assert alphas[c].view(np.uint32) == np.float32(R.alpha).view(np.uint32), (c, alphas[c], R.alpha)
-        assert np.array_equal(scales[:, t0:t1].reshape(-1, d // 16), R.scales), f"chunk {c} scales"
-        assert np.array_equal(codes[:, t0:t1].reshape(-1, d // 2), R.codes), f"chunk {c} codes"
-        deq = oracle.dequantize(R)
-        assert np.array_equal(g32[:, t0:t1].reshape(-1, d), deq), f"chunk {c} fp32 dequantize"
-        assert np.array_equal(g16[:, t0:t1].reshape(-1, d), oracle.bf16_rne(deq)), f"chunk {c} bf16 dequantize"
+    if not many:
+        codes, scales, alphas, g32, g16 = codes[None], scales[None], alphas[None], g32[None], g16[None]
+    for u, refs in enumerate(per):
+        for c, (t0, t1, R) in enumerate(refs):
+            tag = f"tensor {u} chunk {c}"
+            assert alphas[u, c].view(np.uint32) == np.float32(R.alpha).view(np.uint32), (tag, alphas[u, c], R.alpha)
+            assert np.array_equal(scales[u, :, t0:t1].reshape(-1, d // 16), R.scales), f"{tag} scales"
+            assert np.array_equal(codes[u, :, t0:t1].reshape(-1, d // 2), R.codes), f"{tag} codes"
+            deq = oracle.dequantize(R)
+            assert np.array_equal(g32[u, :, t0:t1].reshape(-1, d), deq), f"{tag} fp32 dequantize"
+            assert np.array_equal(g16[u, :, t0:t1].reshape(-1, d), oracle.bf16_rne(deq)), f"{tag} bf16 dequantize"
     return got
 
 
@@ -93,10 +101,28 @@ def test_zero_chunk_and_empty():
     assert e.codes.numel() == 0
 
 
+@pytest.mark.parametrize("tpc", [5, 16, 60])
+def test_two_tensors_in_one_call(tpc):
+    """K and V of a layer as one [2, heads, tokens, d] input: each tensor's
+    chunks get their own scales, alphas [2, n_chunks]."""
+    kv = np.stack((workloads.random_bf16(40 + tpc, (3, 60, 32), 1.0, 0.01),
+                   workloads.random_bf16(41 + tpc, (3, 60, 32), 50.0, 0.01)))   # V larger than K
+    got = _check(kv, tpc, 1)
+    a = got.alphas.cpu().numpy()
+    assert a.shape == (2, (60 + tpc - 1) // tpc) and (a[1] > a[0]).all()
+
+
+def test_two_tensors_handed_amax_fp32():
+    rng = np.random.default_rng(33)
+    kv = rng.standard_normal((2, 2, 40, 48)).astype(np.float32)
+    kv[0, :, 20:] *= 1e-2
+    _check(kv, 20, 0, chunk_amax=True)
+
+
 @pytest.mark.slow
 def test_kv_cache_full_per_chunk():
     """The KV workload [24, 18480, 128] (21 latent frames of 880 tokens) with
-    the pages' 8-frame chunks: chunks of 8, 8 and 5 frames, K and V."""
+    the pages' 8-frame chunks: chunks of 8, 8 and 5 frames, K and V in one
+    call."""
     c = workloads.config4()
-    for name in ("k", "v"):
-        _check(c[name], 8 * 880, 1)
+    _check(np.stack((c["k"], c["v"])), 8 * 880, 1)

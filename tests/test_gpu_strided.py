@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import dev_from_host, host_bits, packed_to_device
+from tests.gpu_helpers import assert_packed_equal, dev_from_host, host_bits, packed_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,47 @@ def test_wgrad_strided(extra):
     torch.cuda.synchronize()
     assert torch.equal(dw, ref)
     assert _pad_untouched(dwbig, k)
+
+
+def _offset_view(host, dtype, offset):
+    """A contiguous device view of `host` that starts `offset` elements into
+    its allocation: element-aligned, not 16-byte aligned."""
+    d = dev_from_host(host)
+    buf = torch.zeros(d.numel() + 16, dtype=dtype, device="cuda")
+    v = buf[offset:offset + d.numel()].view(d.shape)
+    v.copy_(d)
+    return v
+
+
+@pytest.mark.parametrize("dtype,offset", [(torch.bfloat16, 1), (torch.bfloat16, 3), (torch.float32, 1),
+                                          (torch.float32, 2)])
+def test_col16_amax_on_element_aligned_view(dtype, offset):
+    """COL16 takes element-aligned inputs; its in-call amax pass then reads
+    rows element by element instead of in 16-byte vectors."""
+    rows, cols = 96, 200
+    print(f"[case] col16 element-aligned view {dtype} offset={offset}", flush=True)
+    x = np.random.default_rng(60 + offset).standard_normal((rows, cols)).astype(np.float32)
+    x[37, 11] = 9.5                                # the maximum sits mid-tensor
+    host = x if dtype == torch.float32 else workloads.f32_to_bf16_bits(x)
+    v = _offset_view(host, dtype, offset)
+    assert v.data_ptr() % 16 != 0 and v.is_contiguous()
+    got = nv.quantize(v, "col16", "4over6")
+    torch.cuda.synchronize()
+    assert_packed_equal(got, oracle.quantize(host, oracle.COL16, 1), "col16 offset view")
+
+
+@pytest.mark.parametrize("offset", [1, 5])
+def test_wgrad_element_aligned_views(offset):
+    t, n, k = 1040, 96, 160
+    print(f"[case] wgrad element-aligned views offset={offset}", flush=True)
+    rng = np.random.default_rng(200 + offset)
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((t, k)).astype(np.float32))
+    dy = workloads.f32_to_bf16_bits((rng.standard_normal((t, n)) * 1e-3).astype(np.float32))
+    ref = nv.wgrad(dev_from_host(dy), dev_from_host(x), torch.float32)
+    got = nv.wgrad(_offset_view(dy, torch.bfloat16, offset), _offset_view(x, torch.bfloat16, offset),
+                   torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
 
 
 @pytest.mark.parametrize("block", [oracle.ROW16, oracle.TILE16, oracle.COL16])
