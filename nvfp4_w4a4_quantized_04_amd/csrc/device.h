@@ -108,21 +108,63 @@ __device__ __forceinline__ void encode16(const float (&x)[16], float s, float ka
     c1 = w1;
 }
 
-// kappa = RN(1 / RN(s * alpha)) for every E4M3 scale byte b in [0, 128), 0 for
+// RN(a / b) from y = RN(1 / b) without a division: q0 = RN(a * y), then one
+// fma correction q = RN(q0 + RN(a - q0 * b) * y) with the residual exact
+// (Markstein's correction step).  Checked against IEEE division on the CPU
+// over every (fp32 b, bf16 a) pair of significands in [1, 2), 8.4e9 random
+// fp32 pairs, and, for b = 6, every fp32 a whose quotient is normal.  Exact while the residual does not underflow: callers
+// use it only where quotients below 2^-9 end up in E4M3 conversions that map
+// them to zero either way.
+__device__ __forceinline__ float div_rcp(float a, float b, float y)
+{
+    const float q0 = a * y;
+    return __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
+}
+
+// Slot 127 of the kappa table (E4M3 byte 127 is NaN and never a scale: scales
+// are clamped to 448) holds RN(1 / alpha) when the fast quotient m / alpha is
+// exact for every block max that matters (alpha >= 2^-90: a block max m with
+// m / alpha >= 2^-9 is then >= 2^-99, far from the residual's underflow), 0
+// otherwise.
+constexpr int kRcpAlphaSlot = 127;
+
+// kappa = RN(1 / RN(s * alpha)) for every E4M3 scale byte b in [0, 127), 0 for
 // s == 0; built once per workgroup so blocks look it up instead of dividing.
 // Every thread of the workgroup must call it (it synchronizes).
 __device__ __forceinline__ void build_kappa_table(float *tab, float alpha)
 {
     for (int b = threadIdx.x; b < 128; b += blockDim.x) {
-        const float s = __builtin_amdgcn_cvt_f32_fp8(b, 0);
         float k = 0.0f;
-        if (b != 0 && b < 127) {            // byte 127 (NaN) never occurs: scales are clamped to 448
-            const float d = s * alpha;
-            k = 1.0f / d;                   // IEEE division (correctly rounded)
+        if (b == kRcpAlphaSlot) {
+            if (alpha >= 0x1p-90f)
+                k = 1.0f / alpha;           // IEEE division (correctly rounded)
+        } else if (b != 0) {
+            const float d = __builtin_amdgcn_cvt_f32_fp8(b, 0) * alpha;
+            k = 1.0f / d;
         }
         tab[b] = k;
     }
     __syncthreads();
+}
+
+// The two candidate scale bytes of a block with max |x| = m: byte 0 E4M3(mu /
+// 6), byte 1 E4M3(mu / 4), mu = m / alpha (all quotients correctly rounded).
+__device__ __forceinline__ uint32_t block_scale_bytes(float m, float alpha, const float *ktab)
+{
+    const float ra = ktab[kRcpAlphaSlot];
+    float mu;
+    if (ra != 0.0f) {
+        mu = div_rcp(m, alpha, ra);
+    } else {
+        // the division only on this (rare, workgroup-uniform) path: the empty
+        // asm keeps the compiler from computing it on both sides and selecting
+        float mm = m;
+        asm volatile("" : "+v"(mm));
+        mu = mm / alpha;
+    }
+    const float t6 = div_rcp(mu, 6.0f, 1.0f / 6.0f);
+    const float t4 = mu * 0.25f;                 // == RN(mu / 4)
+    return e4m3_put2(t6, t4);                    // byte0: s6, byte1: s4
 }
 
 // Quantize one 1D block of 16 values (RULE4: four-over-six): codes (8 bytes)
@@ -135,10 +177,7 @@ __device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha,
 #pragma unroll
     for (int i = 0; i < 16; i++)
         m = fmaxf(m, fabsf(x[i]));
-    const float mu = m / alpha;
-    const float t6 = mu / 6.0f;
-    const float t4 = mu * 0.25f;                 // == RN(mu / 4)
-    const uint32_t sb = e4m3_put2(t6, t4);       // byte0: s6, byte1: s4
+    const uint32_t sb = block_scale_bytes(m, alpha, ktab);
     const uint32_t b6 = sb & 0xffu, b4 = (sb >> 8) & 0xffu;
     const float s6 = e4m3_get<0>(sb);
     float e6 = 0.0f;
@@ -155,6 +194,19 @@ __device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha,
             sbyte = b4;
         }
     }
+}
+
+// 16-byte load marked non-temporal: the data is streamed through once, so the
+// caches need not keep it (measured faster on the tensor-sized passes).
+__device__ __forceinline__ uint4 load_stream(const uint4 *p)
+{
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+    uint4 v;
+    v.x = __builtin_nontemporal_load(q);
+    v.y = __builtin_nontemporal_load(q + 1);
+    v.z = __builtin_nontemporal_load(q + 2);
+    v.w = __builtin_nontemporal_load(q + 3);
+    return v;
 }
 
 // 16 consecutive elements of row-major input (16-byte aligned).
@@ -212,12 +264,26 @@ __device__ __forceinline__ void rht16(float (&x)[16], uint32_t signs)
 }
 
 // Wave-wide max (64 lanes).
+// v from another lane by a DPP control; lanes of rows outside ROW_MASK get 0
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_or_zero(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Max over the wave of NON-NEGATIVE values (0 is the identity), the same in
+// every lane: butterflies inside each row of 16 lanes (quad permutes, half-row
+// and row mirrors), then the row broadcasts carry rows 0-2 into row 3, and
+// lane 63 is read back as a uniform value.
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_or_zero<0xB1>(v));          // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_or_zero<0x4E>(v));          // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_or_zero<0x141>(v));         // row_half_mirror
+    v = fmaxf(v, dpp_or_zero<0x140>(v));         // row_mirror: every lane holds its row's max
+    v = fmaxf(v, dpp_or_zero<0x142, 0xa>(v));    // row_bcast15 into rows 1 and 3
+    v = fmaxf(v, dpp_or_zero<0x143, 0xc>(v));    // row_bcast31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 }  // namespace nvfp4

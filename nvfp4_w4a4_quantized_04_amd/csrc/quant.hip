@@ -74,43 +74,41 @@ __device__ __forceinline__ float absmax16B(uint4 v, float a)
     return a;
 }
 
-// Partial maxima: workgroup w reduces one contiguous range of the tensor;
-// every thread keeps kAmaxUnroll 16-byte loads in flight per iteration (the
-// last iteration's loads are predicated, not serialized).
-template <typename T>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols,
-                                                       int64_t ldx, bool vec, float *__restrict__ partials)
+// Partial maxima: workgroup w takes the groups w, w + grid, w + 2 grid, ... of
+// TH * U consecutive 16-byte vectors, every thread keeping U loads in flight
+// (the last group's loads are predicated, not serialized); vec: the tensor is
+// contiguous and 16-byte aligned, else rows are read element by element.
+template <typename T, int TH, int U>
+__global__ __launch_bounds__(TH) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                             bool vec, float *__restrict__ partials)
 {
-    __shared__ float red[kAmaxThreads / 64];
+    __shared__ float red[TH / 64];
     float a = 0.0f;
-    if (vec) {                                  // contiguous and 16-byte aligned: flat 16-byte loads
+    if (vec) {
         constexpr int V = 16 / sizeof(T);
         const int64_t n = rows * cols;
         const int64_t nv = n / V;
-        constexpr int64_t kIter = (int64_t)kAmaxThreads * kAmaxUnroll;   // vectors per workgroup iteration
-        const int64_t per_wg = ((nv + gridDim.x - 1) / gridDim.x + kAmaxThreads - 1) / kAmaxThreads * kAmaxThreads;
-        const int64_t beg = (int64_t)blockIdx.x * per_wg;
-        const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
         const uint4 *xv = reinterpret_cast<const uint4 *>(x);
-        for (int64_t base = beg; base < end; base += kIter) {
-            uint4 v[kAmaxUnroll];
+        const int64_t step = (int64_t)gridDim.x * TH * U;
+        for (int64_t g = (int64_t)blockIdx.x * TH * U; g < nv; g += step) {
+            uint4 v[U];
 #pragma unroll
-            for (int u = 0; u < kAmaxUnroll; u++) {
-                const int64_t i = base + u * kAmaxThreads + threadIdx.x;
-                v[u] = i < end ? xv[i] : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < U; u++) {
+                const int64_t i = g + u * TH + threadIdx.x;
+                v[u] = i < nv ? load_stream(xv + i) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < kAmaxUnroll; u++)
+            for (int u = 0; u < U; u++)
                 a = absmax16B<T>(v[u], a);
         }
         // elements past the last whole vector
-        const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-        for (int64_t t = nv * V + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < n; t += stride)
+        const int64_t stride = (int64_t)gridDim.x * TH;
+        for (int64_t t = nv * V + (int64_t)blockIdx.x * TH + threadIdx.x; t < n; t += stride)
             a = fmaxf(a, fabsf(load1(x + t)));
     } else {
         // strided rows: rows spread over workgroups, threads along the row
         for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
-            for (int64_t c = threadIdx.x; c < cols; c += kAmaxThreads)
+            for (int64_t c = threadIdx.x; c < cols; c += TH)
                 a = fmaxf(a, fabsf(load1(x + r * ldx + c)));
     }
     a = wave_max(a);
@@ -120,7 +118,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const T *__restrict__ x, 
     if (threadIdx.x == 0) {
         float b = red[0];
 #pragma unroll
-        for (int w = 1; w < kAmaxThreads / 64; w++)
+        for (int w = 1; w < TH / 64; w++)
             b = fmaxf(b, red[w]);
         partials[blockIdx.x] = b;
     }
@@ -196,7 +194,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
         const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
 #pragma unroll
         for (int u = 0; u < kVec; u++)
-            raw[j][u] = src[u];
+            raw[j][u] = load_stream(src + u);
     }
     const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
@@ -437,8 +435,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_tile16(const T *__restr
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1)
             m = fmaxf(m, __shfl_xor(m, o, 16));
-        const float mu = m / alpha;
-        const uint32_t sb = e4m3_put2(mu / 6.0f, mu * 0.25f);
+        const uint32_t sb = block_scale_bytes(m, alpha, ktab);
         const float s6 = e4m3_get<0>(sb);
         uint32_t c0, c1;
         float er = 0.0f;
@@ -767,7 +764,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__res
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; u++) {
             const int64_t i = base + u * kAmaxThreads + threadIdx.x;
-            v[u] = i < end ? xv[i] : make_uint4(0, 0, 0, 0);
+            v[u] = i < end ? load_stream(xv + i) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; u++)
@@ -814,7 +811,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__r
     const uint4 *p = reinterpret_cast<const uint4 *>(x + b * 16);
 #pragma unroll
     for (int u = 0; u < kVec; u++)
-        raw[u] = p[u];
+        raw[u] = load_stream(p + u);
     const float alpha = alpha_finish(apart, src, n_amax);
     build_kappa_table(ktab, alpha);
     if (blockIdx.x == 0 && h == 0 && threadIdx.x == 0)
@@ -854,28 +851,40 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_kv_chunked(const uint
 
 // ------------------------------------------------------------ launchers
 
-int amax_partials(int64_t rows, int64_t cols)
+int amax_partials(int64_t rows, int64_t cols, bool wide)
 {
     // enough workgroups to cover every CU even for small tensors: about one
-    // 16-byte vector per thread per workgroup, at most kMaxAmaxPartials
+    // 16-byte vector per thread per workgroup, capped
     const int64_t n = rows * cols;
-    const int64_t per_wg = (int64_t)kAmaxThreads * 8;
+    const int64_t per_wg = (int64_t)(wide ? kAmaxWideThreads : kAmaxThreads) * 8;
+    const int64_t cap = wide ? kMaxAmaxSrc : kMaxAmaxPartials;
     int64_t p = (n + per_wg - 1) / per_wg;
     if (p < 1) p = 1;
-    if (p > kMaxAmaxPartials) p = kMaxAmaxPartials;
+    if (p > cap) p = cap;
     return (int)p;
 }
 
 hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
-                       int n_partials, hipStream_t s)
+                       int n_partials, bool wide, hipStream_t s)
 {
     // the flat vector path needs whole 16-byte vectors: entry points that take
     // element-aligned inputs (COL16, WGRAD) fall back to the row loop
     const bool vec = ldx == cols && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-    if (dtype == 1)
-        k_amax<uint16_t><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx, vec, partials);
-    else
-        k_amax<float><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, vec, partials);
+    if (wide) {
+        if (dtype == 1)
+            k_amax<uint16_t, kAmaxWideThreads, 8><<<n_partials, kAmaxWideThreads, 0, s>>>(
+                (const uint16_t *)x, rows, cols, ldx, vec, partials);
+        else
+            k_amax<float, kAmaxWideThreads, 8><<<n_partials, kAmaxWideThreads, 0, s>>>(
+                (const float *)x, rows, cols, ldx, vec, partials);
+    } else {
+        if (dtype == 1)
+            k_amax<uint16_t, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>(
+                (const uint16_t *)x, rows, cols, ldx, vec, partials);
+        else
+            k_amax<float, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>(
+                (const float *)x, rows, cols, ldx, vec, partials);
+    }
     return hipGetLastError();
 }
 
