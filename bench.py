@@ -54,17 +54,23 @@ PEAK_SCLK_MHZ = 2400.0               # the shader clock the published peaks assu
 # HBM bytes per launch of the QKV-shaped GEMM kernel, from rocprofv3 byte
 # counters: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors being what the two
 # counters read for a plain 256 MiB device copy.  They hold for the GEMM
-# source they were taken with only: null once gemm.hip has changed.
+# sources they were taken with only (gemm.hip and the device.h it includes):
+# null once either has changed.
 GEMM_TRAFFIC = {"gemm_src_sha256": "27f763b7e8e99d91cc6181c4646c7cd8c8b64c6e66fb8e6426711a0414d00f01",
                 "bytes_per_launch": 140017664}
 
 
-def gemm_traffic():
+def gemm_src_sha256():
     import hashlib
-    src = os.path.join(ROOT, "nvfp4_w4a4_quantized_04_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()
-    return GEMM_TRAFFIC["bytes_per_launch"] if h == GEMM_TRAFFIC["gemm_src_sha256"] else None
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "device.h"):
+        with open(os.path.join(ROOT, "nvfp4_w4a4_quantized_04_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def gemm_traffic():
+    return GEMM_TRAFFIC["bytes_per_launch"] if gemm_src_sha256() == GEMM_TRAFFIC["gemm_src_sha256"] else None
 
 
 def log(msg):

@@ -109,7 +109,7 @@ int nvfp4_abi_version(void);
 const char *nvfp4_status_string(nvfp4_status_t status);
 
 /* Bytes of workspace nvfp4_quantize / nvfp4_kv_quantize need (amax partial
- * maxima): 4 KiB. */
+ * maxima).  Never more than 4 KiB (currently 1 KiB). */
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 
 /*

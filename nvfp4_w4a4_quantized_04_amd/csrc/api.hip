@@ -74,13 +74,11 @@ nvfp4_status_t do_quantize(const void *x, int x_dtype, int64_t rows, int64_t col
     const float *src = amax;
     int n = 1;
     if (!amax) {
-        // the ROW16 quantizer reduces up to kMaxAmaxSrc partials, the others kMaxAmaxPartials
-        const bool wide = block == NVFP4_ROW16 && rht_signs < 0;
-        n = amax_partials(rows, cols, wide);
+        n = amax_partials(rows, cols);
         hipError_t e = rht_signs >= 0
                            ? launch_amax_col16_rht(x, x_dtype, rows, cols, ldx, (uint32_t)rht_signs, partials, n,
                                                    stream)
-                           : launch_amax(x, x_dtype, rows, cols, ldx, partials, n, wide, stream);
+                           : launch_amax(x, x_dtype, rows, cols, ldx, partials, n, stream);
         if (e != hipSuccess)
             return NVFP4_ERR_LAUNCH;
         src = partials;

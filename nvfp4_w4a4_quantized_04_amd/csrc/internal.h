@@ -10,21 +10,18 @@ namespace nvfp4 {
 
 constexpr int kQuantThreads = 256;      // threads per quantize workgroup
 constexpr int kRowBlocks = 1;           // 16-element blocks per lane in the ROW16 kernel
-constexpr int kAmaxThreads = 1024;      // threads per amax workgroup (at most kMaxAmaxPartials of them)
-constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per amax thread
+constexpr int kAmaxThreads = 1024;      // threads per amax workgroup
+constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per thread of the per-chunk amax pass
 constexpr int kMaxAmaxPartials = 256;   // amax pass: at most this many workgroups
-constexpr int kAmaxWideThreads = 256;   // threads per workgroup of the wide amax pass (ROW16 callers)
+constexpr size_t kAmaxBytes = kMaxAmaxPartials * sizeof(float);
 constexpr int kMaxAmaxSrc = 1024;       // ROW16 quantize: at most this many amax partials (others: 256)
-constexpr size_t kAmaxBytes = kMaxAmaxSrc * sizeof(float);
 
-// number of amax workgroups (= partial maxima) for a rows x cols tensor:
-// wide (the partials feed the ROW16 quantizer) up to kMaxAmaxSrc workgroups of
-// kAmaxWideThreads, else up to kMaxAmaxPartials of kAmaxThreads
-int amax_partials(int64_t rows, int64_t cols, bool wide = false);
+// number of amax workgroups (= partial maxima) for a rows x cols tensor
+int amax_partials(int64_t rows, int64_t cols);
 
 // dtype: 0 fp32, 1 bf16.  block: 0 ROW16, 1 TILE16, 2 COL16.
 hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
-                       int n_partials, bool wide, hipStream_t s);
+                       int n_partials, hipStream_t s);
 
 // amax partials of the COL16 blocks after the random Hadamard transform
 hipError_t launch_amax_col16_rht(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, uint32_t signs,

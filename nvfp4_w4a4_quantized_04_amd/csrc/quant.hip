@@ -851,40 +851,31 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_kv_chunked(const uint
 
 // ------------------------------------------------------------ launchers
 
-int amax_partials(int64_t rows, int64_t cols, bool wide)
+int amax_partials(int64_t rows, int64_t cols)
 {
     // enough workgroups to cover every CU even for small tensors: about one
-    // 16-byte vector per thread per workgroup, capped
+    // 16-byte vector per thread per workgroup, at most kMaxAmaxPartials (more
+    // partials cost the quantizer more than they gain the amax pass)
     const int64_t n = rows * cols;
-    const int64_t per_wg = (int64_t)(wide ? kAmaxWideThreads : kAmaxThreads) * 8;
-    const int64_t cap = wide ? kMaxAmaxSrc : kMaxAmaxPartials;
+    const int64_t per_wg = (int64_t)kAmaxThreads * 8;
     int64_t p = (n + per_wg - 1) / per_wg;
     if (p < 1) p = 1;
-    if (p > cap) p = cap;
+    if (p > kMaxAmaxPartials) p = kMaxAmaxPartials;
     return (int)p;
 }
 
 hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float *partials,
-                       int n_partials, bool wide, hipStream_t s)
+                       int n_partials, hipStream_t s)
 {
     // the flat vector path needs whole 16-byte vectors: entry points that take
     // element-aligned inputs (COL16, WGRAD) fall back to the row loop
     const bool vec = ldx == cols && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-    if (wide) {
-        if (dtype == 1)
-            k_amax<uint16_t, kAmaxWideThreads, 8><<<n_partials, kAmaxWideThreads, 0, s>>>(
-                (const uint16_t *)x, rows, cols, ldx, vec, partials);
-        else
-            k_amax<float, kAmaxWideThreads, 8><<<n_partials, kAmaxWideThreads, 0, s>>>(
-                (const float *)x, rows, cols, ldx, vec, partials);
-    } else {
-        if (dtype == 1)
-            k_amax<uint16_t, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>(
-                (const uint16_t *)x, rows, cols, ldx, vec, partials);
-        else
-            k_amax<float, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>(
-                (const float *)x, rows, cols, ldx, vec, partials);
-    }
+    if (dtype == 1)
+        k_amax<uint16_t, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx,
+                                                                             vec, partials);
+    else
+        k_amax<float, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, vec,
+                                                                          partials);
     return hipGetLastError();
 }
 
@@ -1064,13 +1055,20 @@ hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t tensors,
     const int64_t bpr = d / 16;
     const int64_t longest = tpc < tokens ? tpc : tokens;           // tokens of the longest chunk
     dim3 gq((unsigned)((longest * bpr + kQuantThreads - 1) / kQuantThreads), (unsigned)heads, (unsigned)units);
+    // partials per thread: one up to kQuantThreads of them, else up to four
+    auto go = [&](auto kernel, auto xt) {
+        kernel<<<gq, kQuantThreads, 0, s>>>(xt, k, src, stride, n_amax, codes, scales, alphas);
+    };
     constexpr int NPT = kMaxAmaxSrc / kQuantThreads;
+    const bool one = n_amax <= kQuantThreads;
+    const uint16_t *xh = (const uint16_t *)x;
+    const float *xf = (const float *)x;
     if (dtype == 1) {
-        if (rule) k_quant_kv_chunked<uint16_t, true, NPT><<<gq, kQuantThreads, 0, s>>>((const uint16_t *)x, k, src, stride, n_amax, codes, scales, alphas);
-        else      k_quant_kv_chunked<uint16_t, false, NPT><<<gq, kQuantThreads, 0, s>>>((const uint16_t *)x, k, src, stride, n_amax, codes, scales, alphas);
+        if (rule) one ? go(k_quant_kv_chunked<uint16_t, true, 1>, xh) : go(k_quant_kv_chunked<uint16_t, true, NPT>, xh);
+        else      one ? go(k_quant_kv_chunked<uint16_t, false, 1>, xh) : go(k_quant_kv_chunked<uint16_t, false, NPT>, xh);
     } else {
-        if (rule) k_quant_kv_chunked<float, true, NPT><<<gq, kQuantThreads, 0, s>>>((const float *)x, k, src, stride, n_amax, codes, scales, alphas);
-        else      k_quant_kv_chunked<float, false, NPT><<<gq, kQuantThreads, 0, s>>>((const float *)x, k, src, stride, n_amax, codes, scales, alphas);
+        if (rule) one ? go(k_quant_kv_chunked<float, true, 1>, xf) : go(k_quant_kv_chunked<float, true, NPT>, xf);
+        else      one ? go(k_quant_kv_chunked<float, false, 1>, xf) : go(k_quant_kv_chunked<float, false, NPT>, xf);
     }
     return hipGetLastError();
 }
