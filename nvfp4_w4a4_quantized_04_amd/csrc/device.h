@@ -112,9 +112,9 @@ __device__ __forceinline__ void encode16(const float (&x)[16], float s, float ka
 // fma correction q = RN(q0 + RN(a - q0 * b) * y) with the residual exact
 // (Markstein's correction step).  Checked against IEEE division on the CPU
 // over every (fp32 b, bf16 a) pair of significands in [1, 2), 8.4e9 random
-// fp32 pairs, and, for b = 6, every fp32 a whose quotient is normal.  Exact while the residual does not underflow: callers
-// use it only where quotients below 2^-9 end up in E4M3 conversions that map
-// them to zero either way.
+// fp32 pairs, and, for b = 6, every fp32 a whose quotient is normal.  Exact
+// while the residual does not underflow: callers use it only where quotients
+// below 2^-9 end up in E4M3 conversions that map them to zero either way.
 __device__ __forceinline__ float div_rcp(float a, float b, float y)
 {
     const float q0 = a * y;
@@ -122,11 +122,18 @@ __device__ __forceinline__ float div_rcp(float a, float b, float y)
 }
 
 // Slot 127 of the kappa table (E4M3 byte 127 is NaN and never a scale: scales
-// are clamped to 448) holds RN(1 / alpha) when the fast quotient m / alpha is
-// exact for every block max that matters (alpha >= 2^-90: a block max m with
-// m / alpha >= 2^-9 is then >= 2^-99, far from the residual's underflow), 0
-// otherwise.
+// are clamped to 448) holds RN(1 / (alpha * sc)), sc = alpha_rescale(alpha).
 constexpr int kRcpAlphaSlot = 127;
+
+// Power of two that keeps the residual of div_rcp(m * sc, alpha * sc, ...)
+// clear of underflow for every block max m with m / alpha >= 2^-9 (smaller
+// quotients give E4M3 zero either way): 1 for alpha >= 2^-90, else 2^100.
+// Scaling both operands by a power of two is exact and leaves the quotient
+// unchanged.
+__device__ __forceinline__ float alpha_rescale(float alpha)
+{
+    return alpha >= 0x1p-90f ? 1.0f : 0x1p100f;
+}
 
 // kappa = RN(1 / RN(s * alpha)) for every E4M3 scale byte b in [0, 127), 0 for
 // s == 0; built once per workgroup so blocks look it up instead of dividing.
@@ -136,8 +143,7 @@ __device__ __forceinline__ void build_kappa_table(float *tab, float alpha)
     for (int b = threadIdx.x; b < 128; b += blockDim.x) {
         float k = 0.0f;
         if (b == kRcpAlphaSlot) {
-            if (alpha >= 0x1p-90f)
-                k = 1.0f / alpha;           // IEEE division (correctly rounded)
+            k = 1.0f / (alpha * alpha_rescale(alpha));     // IEEE division (correctly rounded)
         } else if (b != 0) {
             const float d = __builtin_amdgcn_cvt_f32_fp8(b, 0) * alpha;
             k = 1.0f / d;
@@ -148,20 +154,13 @@ __device__ __forceinline__ void build_kappa_table(float *tab, float alpha)
 }
 
 // The two candidate scale bytes of a block with max |x| = m: byte 0 E4M3(mu /
-// 6), byte 1 E4M3(mu / 4), mu = m / alpha (all quotients correctly rounded).
+// 6), byte 1 E4M3(mu / 4), mu = m / alpha, with the bytes IEEE division would
+// give.  Non-finite quotients (alpha 0, infinite m) come out NaN where the
+// division gives infinity; the 448 clamp maps both to the same byte.
 __device__ __forceinline__ uint32_t block_scale_bytes(float m, float alpha, const float *ktab)
 {
-    const float ra = ktab[kRcpAlphaSlot];
-    float mu;
-    if (ra != 0.0f) {
-        mu = div_rcp(m, alpha, ra);
-    } else {
-        // the division only on this (rare, workgroup-uniform) path: the empty
-        // asm keeps the compiler from computing it on both sides and selecting
-        float mm = m;
-        asm volatile("" : "+v"(mm));
-        mu = mm / alpha;
-    }
+    const float sc = alpha_rescale(alpha);
+    const float mu = div_rcp(m * sc, alpha * sc, ktab[kRcpAlphaSlot]);
     const float t6 = div_rcp(mu, 6.0f, 1.0f / 6.0f);
     const float t4 = mu * 0.25f;                 // == RN(mu / 4)
     return e4m3_put2(t6, t4);                    // byte0: s6, byte1: s4
