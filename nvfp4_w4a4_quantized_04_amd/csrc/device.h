@@ -111,10 +111,10 @@ __device__ __forceinline__ void encode16(const float (&x)[16], float s, float ka
 // RN(a / b) from y = RN(1 / b) without a division: q0 = RN(a * y), then one
 // fma correction q = RN(q0 + RN(a - q0 * b) * y) with the residual exact
 // (Markstein's correction step).  Checked against IEEE division on the CPU
-// over every (fp32 b, bf16 a) pair of significands in [1, 2), 8.4e9 random
-// fp32 pairs, and, for b = 6, every fp32 a whose quotient is normal.  Exact
-// while the residual does not underflow: callers use it only where quotients
-// below 2^-9 end up in E4M3 conversions that map them to zero either way.
+// for all 2^46 pairs of fp32 significands in [1, 2) and, for b = 6, every
+// fp32 a whose quotient is normal.  Exact while the residual does not
+// underflow: callers use it only where quotients below 2^-9 end up in E4M3
+// conversions that map them to zero either way.
 __device__ __forceinline__ float div_rcp(float a, float b, float y)
 {
     const float q0 = a * y;
