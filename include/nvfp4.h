@@ -112,6 +112,12 @@ const char *nvfp4_status_string(nvfp4_status_t status);
  * maxima).  Never more than 4 KiB (currently 1 KiB). */
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 
+/* The same figure under the name of the scope table's helper list: the
+ * workspace of one single-tensor quantize call (nvfp4_quantize,
+ * nvfp4_kv_quantize).  The fused and chunked calls have their own size
+ * helpers. */
+size_t nvfp4_workspace_size(int64_t rows, int64_t cols);
+
 /*
  * nvfp4_quantize -- quantize x [rows][cols] (row stride ldx elements,
  * dtype NVFP4_F32 or NVFP4_BF16) into NVFP4.

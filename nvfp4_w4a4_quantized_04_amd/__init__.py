@@ -59,6 +59,8 @@ def _load():
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_quantize_workspace_size.restype = sz
     L.nvfp4_quantize_workspace_size.argtypes = [i64, i64]
+    L.nvfp4_workspace_size.restype = sz
+    L.nvfp4_workspace_size.argtypes = [i64, i64]
     L.nvfp4_quantize.restype = i32
     L.nvfp4_quantize.argtypes = [P, i32, i64, i64, i64, i32, i32, P, P, P, P, P, sz, P]
     L.nvfp4_dequantize.restype = i32
@@ -103,7 +105,8 @@ def _load():
 
 lib = _load()
 
-EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_quantize",
+EXPORTED = ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_workspace_size", "nvfp4_workspace_size",
+            "nvfp4_quantize",
             "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_kv_quantize", "nvfp4_linear_workspace_size",
             "nvfp4_linear", "nvfp4_wgrad_workspace_size", "nvfp4_wgrad", "nvfp4_transpose_tile16",
             "nvfp4_quantize_col16_rht", "nvfp4_kv_smooth_workspace_size", "nvfp4_kv_quantize_smoothed",

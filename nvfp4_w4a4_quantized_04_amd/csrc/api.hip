@@ -128,6 +128,8 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols)
     return kAmaxBytes;
 }
 
+size_t nvfp4_workspace_size(int64_t rows, int64_t cols) { return nvfp4_quantize_workspace_size(rows, cols); }
+
 nvfp4_status_t nvfp4_quantize(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx, int block,
                               int rule, const float *amax, uint8_t *codes, uint8_t *scales, float *alpha,
                               void *workspace, size_t workspace_bytes, hipStream_t stream)

@@ -32,6 +32,12 @@ def test_library_exports_every_declared_symbol():
     assert m.lib.nvfp4_abi_version() == 1
 
 
+def test_workspace_size_helper_names_agree():
+    import nvfp4_w4a4_quantized_04_amd as m
+    for rows, cols in ((16, 16), (2640, 3072), (443520, 128)):
+        assert m.lib.nvfp4_workspace_size(rows, cols) == m.lib.nvfp4_quantize_workspace_size(rows, cols) > 0
+
+
 def test_status_strings():
     import nvfp4_w4a4_quantized_04_amd as m
     for st in range(8):
