@@ -290,8 +290,19 @@ def bench_kv(nv, workloads, iters):
                       device="cuda")
     torch.cuda.synchronize()
 
+    # the chunks' maxima as the pages' streaming inference has them: each
+    # chunk's K and V come out of that chunk's projection, whose epilogue
+    # reports max |C| (one read per call)
+    nch = (tokens + tpc - 1) // tpc
+    cam = [torch.stack([p[u, :, c * tpc:(c + 1) * tpc].float().abs().amax() for u in range(2) for c in range(nch)])
+           .contiguous() for p in pairs]
+    torch.cuda.synchronize()
+
     def qc(i):
         nv.kv_quantize_chunked(pairs[i % 2], tpc, out=cpk[i % 2], workspace=cws)
+
+    def qc1(i):
+        nv.kv_quantize_chunked(pairs[i % 2], tpc, out=cpk[i % 2], chunk_amax=cam[i % 2])
 
     def dqc(i):
         nv.kv_dequantize_chunked(cpk[i % 2], torch.bfloat16, out=cy[i % 2])
@@ -300,6 +311,7 @@ def bench_kv(nv, workloads, iters):
     t1 = time_events(q1, iters)
     tdq = time_events(dq, iters)
     tqc = time_events(qc, iters) / 2                  # per tensor: each call quantizes K and V
+    tqc1 = time_events(qc1, iters) / 2
     tdqc = time_events(dqc, iters) / 2
     bytes_q = n * 2 + n * 9 / 16 + 4          # read bf16, write codes + scales + alpha
     bytes_dq = n * 9 / 16 + 4 + n * 2
@@ -309,9 +321,9 @@ def bench_kv(nv, workloads, iters):
         return round(gbps, 1), round(gbps / HBM_PEAK_GBPS, 4)
 
     r2, r1, rd = rate(bytes_q, t2), rate(bytes_q, t1), rate(bytes_dq, tdq)
-    nch = (tokens + tpc - 1) // tpc
     rc, rdc = rate(bytes_q + 4 * (nch - 1), tqc), rate(bytes_dq + 4 * (nch - 1), tdqc)
-    del sets, pairs, cpk, cy
+    rc1 = rate(bytes_q + 4 * (nch - 1), tqc1)
+    del sets, pairs, cpk, cy, cam
     torch.cuda.empty_cache()
     win = bench_kv_window(nv, iters)
     return {
@@ -323,9 +335,12 @@ def bench_kv(nv, workloads, iters):
         "per_chunk_alpha": {
             "tokens_per_chunk": tpc, "chunks": nch,
             "quantize_ms_per_tensor": round(tqc, 5), "quantize_GBps": rc[0], "quantize_frac_hbm": rc[1],
+            "quantize_1pass_ms_per_tensor": round(tqc1, 5), "quantize_1pass_GBps": rc1[0],
+            "quantize_1pass_frac_hbm": rc1[1],
             "dequantize_ms_per_tensor": round(tdqc, 5), "dequantize_GBps": rdc[0], "dequantize_frac_hbm": rdc[1],
             "note": "one global scale per 8-frame chunk of the 21-frame tensor, K and V and all their chunks "
-                    "in one call (amax partials per tensor and chunk, then the quantizer); time per tensor is "
+                    "in one call (amax partials per tensor and chunk, then the quantizer; quantize_1pass: the "
+                    "chunks' maxima handed in, as each chunk's projection reports them); time per tensor is "
                     "half the call"},
         "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
         "note": "GB/s = algorithmic bytes / event time per call, three rotating 113.5 MB tensors; quantize = amax "
