@@ -279,6 +279,11 @@ def bench_kv(nv, workloads, iters):
         kv, p, y, ws, am = sets[i % len(sets)]
         nv.dequantize(p, torch.bfloat16, out=y)
 
+    def copy(i):
+        # context: a plain device copy of one 113.5 MB tensor (torch), the
+        # rate a read-and-write stream reaches on this machine
+        sets[i % len(sets)][2].view(heads, tokens, d).copy_(sets[(i + 1) % len(sets)][0])
+
     # the pages' granularity: one global scale per 8-frame chunk (7040 tokens:
     # chunks of 8, 8 and 5 frames) of K and of V, both tensors and all their
     # chunks in one call; two such [2, heads, tokens, d] pairs alternate
@@ -310,6 +315,7 @@ def bench_kv(nv, workloads, iters):
     t2 = time_events(q2, iters)
     t1 = time_events(q1, iters)
     tdq = time_events(dq, iters)
+    tcp = time_events(copy, iters)
     tqc = time_events(qc, iters) / 2                  # per tensor: each call quantizes K and V
     tqc1 = time_events(qc1, iters) / 2
     tdqc = time_events(dqc, iters) / 2
@@ -342,6 +348,10 @@ def bench_kv(nv, workloads, iters):
                     "in one call (amax partials per tensor and chunk, then the quantizer; quantize_1pass: the "
                     "chunks' maxima handed in, as each chunk's projection reports them); time per tensor is "
                     "half the call"},
+        "context_device_copy": {"ms": round(tcp, 5), "GBps": round(2 * n * 2 / (tcp * 1e-3) / 1e9, 1),
+                                "frac_hbm": round(2 * n * 2 / (tcp * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                "note": "torch copy of one bf16 tensor of the same size (read + write): the "
+                                        "rate a plain read-and-write stream reaches here, context only"},
         "algorithmic_bytes_per_tensor": {"quantize": bytes_q, "dequantize": bytes_dq},
         "note": "GB/s = algorithmic bytes / event time per call, three rotating 113.5 MB tensors; quantize = amax "
                 "pass inside the call (two reads of the tensor), quantize_1pass = amax supplied by the producing "
