@@ -742,8 +742,9 @@ __device__ __forceinline__ int64_t chunk_len(const KvChunks &k, int z)
 }
 
 // Partial maxima: workgroup (p, h, z) reduces part p of the head-h segment of
-// unit z into partials[z * heads * pseg + h * pseg + p] (same loop shape as
-// k_amax: eight 16-byte loads in flight per thread).
+// unit z into partials[z * heads * pseg + h * pseg + p]: one contiguous range
+// of the segment per workgroup, eight streaming 16-byte loads in flight per
+// thread.
 template <typename T>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__restrict__ x, KvChunks k,
                                                                   float *__restrict__ partials)
