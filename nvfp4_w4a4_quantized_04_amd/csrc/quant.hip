@@ -496,29 +496,16 @@ __device__ __forceinline__ void decode16(uint32_t c0, uint32_t c1, float s, floa
 }
 
 // ROW16 / TILE16: one lane per 16-element row segment.
-template <typename O, bool TILE>
-__global__ __launch_bounds__(kQuantThreads) void k_dequant_rows(const uint8_t *__restrict__ codes,
-                                                                const uint8_t *__restrict__ scales,
-                                                                const float *__restrict__ alpha_p, int64_t rows,
-                                                                int64_t bpr, O *__restrict__ y, int64_t ldy)
+// The 16 outputs of a lane as 16-byte pieces: 2 (bf16, round to nearest even)
+// or 4 (fp32).
+template <typename O>
+__device__ __forceinline__ void pack16(const float (&v)[16], uint4 (&pc)[sizeof(O)])
 {
-    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-    if (b >= rows * bpr)
-        return;
-    const float alpha = *alpha_p;
-    // 32-bit division while the block index fits (every tensor here does)
-    const int64_t r = b < 0x7fffffff ? (int64_t)((uint32_t)b / (uint32_t)bpr) : b / bpr;
-    const int64_t cb = b - r * bpr;
-    const uint2 c = *reinterpret_cast<const uint2 *>(codes + b * 8);
-    const int64_t soff = TILE ? (r / 16) * bpr + cb : b;
-    const float s = e4m3_get<0>(scales[soff]);
-    float v[16];
-    decode16(c.x, c.y, s, alpha, v);
-    O *out = y + r * ldy + cb * 16;
-    if (sizeof(O) == 4) {
+    if constexpr (sizeof(O) == 4) {
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            reinterpret_cast<float4 *>(out)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+            pc[i] = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]), __float_as_uint(v[4 * i + 2]),
+                               __float_as_uint(v[4 * i + 3]));
     } else {
         uint32_t w[8];
 #pragma unroll
@@ -526,8 +513,70 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_rows(const uint8_t *_
             __bf16 lo = (__bf16)v[2 * i], hi = (__bf16)v[2 * i + 1];
             w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
-        reinterpret_cast<uint4 *>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4 *>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        pc[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        pc[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
+// Workgroup-wide store of one 16-element output row per lane, the rows of
+// consecutive lanes consecutive in memory from `out` on: the pieces go
+// through LDS so that every store instruction of a wave writes one contiguous
+// 1 KiB run (a lane's own 32 or 64 bytes at a 32- or 64-byte stride store
+// measurably slower).  n_valid: how many of the workgroup's rows exist (a
+// prefix).  Every thread of the workgroup must call it (it synchronizes).
+template <typename O>
+__device__ __forceinline__ void store16_staged(O *out, const float (&v)[16], int n_valid, uint4 *stage)
+{
+    constexpr int P = (int)sizeof(O);                   // 16-byte pieces per row
+    uint4 pc[P];
+    pack16<O>(v, pc);
+#pragma unroll
+    for (int j = 0; j < P; j++)
+        stage[threadIdx.x * P + j] = pc[j];
+    __syncthreads();
+    const int w0 = (int)(threadIdx.x & ~63u) * P;       // first piece of this wave's rows
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        const int piece = w0 + j * 64 + lane;
+        if (piece < n_valid * P)
+            reinterpret_cast<uint4 *>(out)[piece] = stage[piece];
+    }
+}
+
+template <typename O, bool TILE>
+__global__ __launch_bounds__(kQuantThreads) void k_dequant_rows(const uint8_t *__restrict__ codes,
+                                                                const uint8_t *__restrict__ scales,
+                                                                const float *__restrict__ alpha_p, int64_t rows,
+                                                                int64_t bpr, O *__restrict__ y, int64_t ldy)
+{
+    __shared__ uint4 stage[kQuantThreads * sizeof(O)];
+    const int64_t nb = rows * bpr;
+    const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads;
+    const int64_t b = b0 + threadIdx.x;
+    const bool flat = !TILE && ldy == bpr * 16;
+    if (!flat && b >= nb)
+        return;
+    const int64_t bc = b < nb ? b : nb - 1;             // past the end: re-read the last block, store nothing
+    const float alpha = *alpha_p;
+    // 32-bit division while the block index fits (every tensor here does)
+    const int64_t r = bc < 0x7fffffff ? (int64_t)((uint32_t)bc / (uint32_t)bpr) : bc / bpr;
+    const int64_t cb = bc - r * bpr;
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + bc * 8);
+    const int64_t soff = TILE ? (r / 16) * bpr + cb : bc;
+    const float s = e4m3_get<0>(scales[soff]);
+    float v[16];
+    decode16(c.x, c.y, s, alpha, v);
+    if (flat) {                                         // workgroup-uniform
+        const int64_t left = nb - b0;
+        store16_staged<O>(y + b0 * 16, v, left < kQuantThreads ? (int)left : kQuantThreads, stage);
+    } else {
+        uint4 pc[sizeof(O)];
+        pack16<O>(v, pc);
+        uint4 *out = reinterpret_cast<uint4 *>(y + r * ldy + cb * 16);
+#pragma unroll
+        for (int j = 0; j < (int)sizeof(O); j++)
+            out[j] = pc[j];
     }
 }
 
