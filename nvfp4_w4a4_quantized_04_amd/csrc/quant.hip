@@ -702,24 +702,16 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_quant_smoothed(const T *__
 // dequantized together into the window buffer): segment i contributes rows
 // [first, first + count) of its chunk, in segment order.  One lane per 16
 // elements; the vector's mean is added back for smoothed keys.
-// Store 16 fp32 values as fp32 or bf16 (round to nearest even).
+// Store 16 fp32 values as fp32 or bf16 (round to nearest even), one lane's
+// own 32 or 64 bytes.
 template <typename O>
 __device__ __forceinline__ void store16(O *out, const float (&v)[16])
 {
-    if (sizeof(O) == 4) {
+    uint4 pc[sizeof(O)];
+    pack16<O>(v, pc);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            reinterpret_cast<float4 *>(out)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    } else {
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            __bf16 lo = (__bf16)v[2 * i], hi = (__bf16)v[2 * i + 1];
-            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        reinterpret_cast<uint4 *>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4 *>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    }
+    for (int j = 0; j < (int)sizeof(O); j++)
+        reinterpret_cast<uint4 *>(out)[j] = pc[j];
 }
 
 // Each workgroup serves one segment (the host gives segment i the workgroups
@@ -728,6 +720,7 @@ __device__ __forceinline__ void store16(O *out, const float (&v)[16])
 template <typename O>
 __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *__restrict__ y, int64_t ldy)
 {
+    __shared__ uint4 stage[kQuantThreads * sizeof(O)];
     const int wg = blockIdx.x;
     int si = 0;
     while (si + 1 < a.n && wg >= a.seg[si + 1].wg0)
@@ -735,11 +728,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *
     const KvSegmentDev &sg = a.seg[si];
     const uint32_t bpr = (uint32_t)a.bpr;
     // count * bpr < 2^31 (checked by the caller): 32-bit index arithmetic
-    const uint32_t local = (uint32_t)(wg - sg.wg0) * kQuantThreads + threadIdx.x;
-    if (local >= (uint32_t)sg.count * bpr)
+    const uint32_t n = (uint32_t)sg.count * bpr;
+    const uint32_t local0 = (uint32_t)(wg - sg.wg0) * kQuantThreads;
+    const uint32_t local = local0 + threadIdx.x;
+    // dense output rows: the segment's rows are one contiguous run of the
+    // window buffer, stored through LDS (workgroup-uniform)
+    const bool flat = ldy == a.bpr * 16;
+    if (!flat && local >= n)
         return;
-    const uint32_t r = local / bpr;
-    const int cb = (int)(local - r * bpr);
+    const uint32_t lc = local < n ? local : n - 1;   // past the end: re-read the last block, store nothing
+    const uint32_t r = lc / bpr;
+    const int cb = (int)(lc - r * bpr);
     const int64_t v = sg.first + r;
     const int64_t blk = v * bpr + cb;
     // the key mean is loaded with the codes and the scale (a segment without
@@ -757,7 +756,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_window(KvWindowArgs a, O *
         for (int i = 0; i < 16; i++)
             val[i] = val[i] + m;
     }
-    store16(y + (sg.out_row + r) * ldy + cb * 16, val);
+    if (flat) {
+        const uint32_t left = n - local0;
+        store16_staged<O>(y + sg.out_row * ldy + (int64_t)local0 * 16, val,
+                          left < (uint32_t)kQuantThreads ? (int)left : kQuantThreads, stage);
+    } else {
+        store16(y + (sg.out_row + r) * ldy + cb * 16, val);
+    }
 }
 
 // ------------------------------------- KV cache: one global scale per chunk
@@ -884,19 +889,21 @@ __global__ __launch_bounds__(kQuantThreads) void k_dequant_kv_chunked(const uint
                                                                       const float *__restrict__ alphas, KvChunks k,
                                                                       int64_t nblocks, O *__restrict__ y)
 {
-    const int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-    if (b >= nblocks)
-        return;
+    __shared__ uint4 stage[kQuantThreads * sizeof(O)];
+    const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads;
+    const int64_t b = b0 + threadIdx.x;
+    const int64_t bc = b < nblocks ? b : nblocks - 1;        // past the end: re-read the last block, store nothing
     const int64_t bpr = k.d / 16;
-    const int64_t row = b / bpr;
+    const int64_t row = bc / bpr;
     const int64_t ht = row / k.tokens;                        // tensor * heads + head
     const int64_t t = row - ht * k.tokens;
-    const uint2 cw = *reinterpret_cast<const uint2 *>(codes + b * 8);
-    const float s = e4m3_get<0>(scales[b]);
+    const uint2 cw = *reinterpret_cast<const uint2 *>(codes + bc * 8);
+    const float s = e4m3_get<0>(scales[bc]);
     const float alpha = alphas[(ht / k.heads) * k.nch + t / k.tpc];
     float v[16];
     decode16(cw.x, cw.y, s, alpha, v);
-    store16(y + b * 16, v);
+    const int64_t left = nblocks - b0;
+    store16_staged<O>(y + b0 * 16, v, left < kQuantThreads ? (int)left : kQuantThreads, stage);
 }
 
 // ------------------------------------------------------------ launchers
