@@ -31,6 +31,7 @@
 // Workgroup tile (64 TM) x (64 TN), BK = 64; consumer wave tile (32 TM) x (32 TN).
 #include "internal.h"
 
+#include <cmath>
 #include <type_traits>
 
 namespace nvfp4 {
@@ -49,6 +50,7 @@ struct GemmArgs {
     int M, N, K;
     int a2d, b2d;
     int tiles_m, tiles_n;
+    int band;       // tile rows per band of the tile order (see the kernel)
     int c_bf16;
     int vec_ok;     // C pointer and ldc allow 4-element vector stores
     int stage_ok;   // bf16 C, 16-byte aligned rows, N % 8 == 0: epilogue staged through LDS
@@ -231,15 +233,21 @@ void k_gemm_nvfp4(GemmArgs g)
     const int wave = tid >> 6;
 
     // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-    // L2.  Renumber so consecutive logical ids run on one XCD, then walk the
-    // tiles down a column (tm fastest) so an XCD shares weight tiles.
+    // L2.  Renumber so consecutive logical ids run on one XCD.  Logical ids
+    // walk bands of g.band tile rows, column after column (tm fastest inside a
+    // band): the tiles an XCD runs at once then form a compact block of about
+    // band x (32 / band) tiles, whose distinct A and B panels are what its L2
+    // fetches per K step.
     const int nwg = g.tiles_m * g.tiles_n;
     const int per_xcd = (nwg + 7) / 8;
     const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
     const int full = nwg - (per_xcd - 1) * 8;              // XCDs that host per_xcd workgroups
     const int lid = xcd < full ? xcd * per_xcd + idx : full * per_xcd + (xcd - full) * (per_xcd - 1) + idx;
-    const int tn = lid / g.tiles_m;
-    const int tm = lid - tn * g.tiles_m;
+    const int band = lid / (g.band * g.tiles_n);
+    const int in_band = lid - band * g.band * g.tiles_n;
+    const int band_rows = min(g.band, g.tiles_m - band * g.band);   // the last band may be shorter
+    const int tn = in_band / band_rows;
+    const int tm = band * g.band + (in_band - tn * band_rows);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (g.K + kBK - 1) / kBK;
 
@@ -550,6 +558,11 @@ static hipError_t launch_tm_tn(GemmArgs &g, hipStream_t s)
 {
     g.tiles_m = (g.M + 64 * TM - 1) / (64 * TM);
     g.tiles_n = (g.N + 64 * TN - 1) / (64 * TN);
+    // Band height: the 32 tiles an XCD (32 CUs) runs at once fetch the fewest
+    // panel rows per K step as a block of h x (32 / h) tiles with
+    // h * BM ~ (32 / h) * BN.
+    const int h = (int)std::lround(std::sqrt(32.0 * TN / TM));
+    g.band = h < 1 ? 1 : (h > g.tiles_m ? g.tiles_m : h);
     const int64_t grid = (int64_t)g.tiles_m * g.tiles_n;
     if (grid * 512 > (int64_t)0xFFFFFFFF)
         return hipErrorInvalidConfiguration;   // a dispatch counts its work-items in 32 bits
