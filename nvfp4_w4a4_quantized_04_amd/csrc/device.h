@@ -208,6 +208,26 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p)
     return v;
 }
 
+// Stores marked non-temporal, for outputs the writing kernel does not read
+// back (measured faster for the quantizers' packed codes and scales and for
+// the GEMM's C tile).
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// one block's 8 code bytes (8-byte aligned) and its scale byte
+__device__ __forceinline__ void store_block_stream(uint8_t *codes8, uint8_t *scale, uint32_t c0, uint32_t c1,
+                                                   uint32_t sb)
+{
+    __builtin_nontemporal_store(u32x2v{c0, c1}, reinterpret_cast<u32x2v *>(codes8));
+    __builtin_nontemporal_store((uint8_t)sb, scale);
+}
+
+// 16 bytes (16-byte aligned)
+__device__ __forceinline__ void store16_stream(void *p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v *>(p));
+}
+
 // 16 consecutive elements of row-major input (16-byte aligned).
 __device__ __forceinline__ void load16(const uint16_t *p, float (&x)[16])
 {

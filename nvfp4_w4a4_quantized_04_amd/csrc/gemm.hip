@@ -196,7 +196,7 @@ __device__ __forceinline__ void read_frags(const uint8_t *stage, int a_frag, int
 __host__ __device__ constexpr int c_pitch(int bn) { return bn * 2 + 16; }
 
 // All 512 threads copy the staged bf16 tile [BM][BN] to C, 16 bytes per
-// store, consecutive threads along a row.
+// non-temporal store, consecutive threads along a row.
 template <int BM, int BN>
 __device__ __forceinline__ void store_staged_c(const GemmArgs &g, const uint8_t *lds, int m0, int n0, int tid)
 {
@@ -209,7 +209,7 @@ __device__ __forceinline__ void store_staged_c(const GemmArgs &g, const uint8_t 
         const int row = m0 + r, col = n0 + c * 8;
         if (row < g.M && col < g.N) {
             const uint4 v = *reinterpret_cast<const uint4 *>(lds + r * c_pitch(BN) + c * 16);
-            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(g.c) + (int64_t)row * g.ldc + col) = v;
+            store16_stream(reinterpret_cast<uint16_t *>(g.c) + (int64_t)row * g.ldc + col, v);
         }
     }
 }

@@ -208,8 +208,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
             unpack16<T>(raw[j], v);
             uint32_t c0, c1, sb;
             quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
-            *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
-            scales[b] = (uint8_t)sb;
+            store_block_stream(codes + b * 8, scales + b, c0, c1, sb);
         }
     }
 }
@@ -521,9 +520,10 @@ __device__ __forceinline__ void pack16(const float (&v)[16], uint4 (&pc)[sizeof(
 // Workgroup-wide store of one 16-element output row per lane, the rows of
 // consecutive lanes consecutive in memory from `out` on: the pieces go
 // through LDS so that every store instruction of a wave writes one contiguous
-// 1 KiB run (a lane's own 32 or 64 bytes at a 32- or 64-byte stride store
-// measurably slower).  n_valid: how many of the workgroup's rows exist (a
-// prefix).  Every thread of the workgroup must call it (it synchronizes).
+// 1 KiB run, non-temporal (a lane's own 32 or 64 bytes at a 32- or 64-byte
+// stride store measurably slower, and so do the same runs as ordinary
+// stores).  n_valid: how many of the workgroup's rows exist (a prefix).
+// Every thread of the workgroup must call it (it synchronizes).
 template <typename O>
 __device__ __forceinline__ void store16_staged(O *out, const float (&v)[16], int n_valid, uint4 *stage)
 {
@@ -540,7 +540,7 @@ __device__ __forceinline__ void store16_staged(O *out, const float (&v)[16], int
     for (int j = 0; j < P; j++) {
         const int piece = w0 + j * 64 + lane;
         if (piece < n_valid * P)
-            reinterpret_cast<uint4 *>(out)[piece] = stage[piece];
+            store16_stream(reinterpret_cast<uint4 *>(out) + piece, stage[piece]);
     }
 }
 
@@ -691,8 +691,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_kv_quant_smoothed(const T *__
         f[i] = f[i] - mean;
     uint32_t c0, c1, sb;
     quant_block16<RULE4>(f, alpha, ktab, c0, c1, sb);
-    *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
-    scales[b] = (uint8_t)sb;
+    store_block_stream(codes + b * 8, scales + b, c0, c1, sb);
 }
 
 // ------------------------------------------------ KV cache: window dequantize
@@ -876,8 +875,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__r
         unpack16<T>(raw, v);
         uint32_t c0, c1, sb;
         quant_block16<RULE4>(v, alpha, ktab, c0, c1, sb);
-        *reinterpret_cast<uint2 *>(codes + b * 8) = make_uint2(c0, c1);
-        scales[b] = (uint8_t)sb;
+        store_block_stream(codes + b * 8, scales + b, c0, c1, sb);
     }
 }
 
