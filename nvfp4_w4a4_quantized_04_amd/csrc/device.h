@@ -196,23 +196,19 @@ __device__ __forceinline__ void quant_block16(const float (&x)[16], float alpha,
 }
 
 // 16-byte load marked non-temporal: the data is streamed through once, so the
-// caches need not keep it (measured faster on the tensor-sized passes).
+// caches need not keep it (measured faster on the tensor-sized passes).  One
+// vector load, so that it stays one 16-byte instruction.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const uint4 *p)
 {
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-    uint4 v;
-    v.x = __builtin_nontemporal_load(q);
-    v.y = __builtin_nontemporal_load(q + 1);
-    v.z = __builtin_nontemporal_load(q + 2);
-    v.w = __builtin_nontemporal_load(q + 3);
-    return v;
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Stores marked non-temporal, for outputs the writing kernel does not read
 // back (measured faster for the quantizers' packed codes and scales and for
 // the GEMM's C tile).
 typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 // one block's 8 code bytes (8-byte aligned) and its scale byte
 __device__ __forceinline__ void store_block_stream(uint8_t *codes8, uint8_t *scale, uint32_t c0, uint32_t c1,
