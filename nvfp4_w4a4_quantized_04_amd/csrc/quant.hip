@@ -779,19 +779,22 @@ struct KvChunks {
     int64_t heads;
     int nch;                  // chunks per tensor
     int pseg;                 // amax workgroups per (unit, head) segment
+    uint64_t nch_magic;       // ceil(2^32 / nch): z / nch == (z * nch_magic) >> 32 for every z < 2^16
 };
 
-// first row of the head-h segment of unit z
-__device__ __forceinline__ int64_t unit_row0(const KvChunks &k, int z, int h)
-{
-    const int u = z / k.nch, c = z - u * k.nch;
-    return ((int64_t)u * k.heads + h) * k.tokens + (int64_t)c * k.tpc;
-}
+inline uint64_t kv_nch_magic(int64_t nch) { return ((1ull << 32) + (uint64_t)nch - 1) / (uint64_t)nch; }
 
-__device__ __forceinline__ int64_t chunk_len(const KvChunks &k, int z)
+// The head-h segment of unit z (z < 2^16): its first row and its row count.
+// The unit's tensor and chunk come from a multiply and shift (checked against
+// division for every z < 2^16 and every chunk count below 2^16) instead of an
+// integer division, which would hold up the workgroup's first loads.
+__device__ __forceinline__ void unit_segment(const KvChunks &k, int z, int h, int64_t &row0, int64_t &len)
 {
-    const int64_t t0 = (int64_t)(z % k.nch) * k.tpc;
-    return k.tokens - t0 < k.tpc ? k.tokens - t0 : k.tpc;
+    const int u = (int)(((uint64_t)(uint32_t)z * k.nch_magic) >> 32);
+    const int c = z - u * k.nch;
+    const int64_t t0 = (int64_t)c * k.tpc;
+    len = k.tokens - t0 < k.tpc ? k.tokens - t0 : k.tpc;
+    row0 = ((int64_t)u * k.heads + h) * k.tokens + t0;
 }
 
 // Partial maxima: workgroup (p, h, z) reduces part p of the head-h segment of
@@ -805,9 +808,10 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_kv_chunked(const T *__res
     __shared__ float red[kAmaxThreads / 64];
     constexpr int V = 16 / sizeof(T);
     const int p = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
-    const int64_t len = chunk_len(k, z);
+    int64_t row0, len;
+    unit_segment(k, z, h, row0, len);
     const int64_t nv = len * k.d / V;                                   // d % 16 == 0: whole vectors
-    const uint4 *xv = reinterpret_cast<const uint4 *>(x + unit_row0(k, z, h) * k.d);
+    const uint4 *xv = reinterpret_cast<const uint4 *>(x + row0 * k.d);
     const int64_t per_wg = ((nv + k.pseg - 1) / k.pseg + kAmaxThreads - 1) / kAmaxThreads * kAmaxThreads;
     const int64_t beg = (int64_t)p * per_wg;
     const int64_t end = beg + per_wg < nv ? beg + per_wg : nv;
@@ -851,13 +855,15 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_kv_chunked(const T *__r
     __shared__ float ktab[128];
     const int h = blockIdx.y, z = blockIdx.z;
     const int64_t bpr = k.d / 16;
-    const int64_t nb = chunk_len(k, z) * bpr;                 // blocks of this segment
+    int64_t row0, len;
+    unit_segment(k, z, h, row0, len);
+    const int64_t nb = len * bpr;                             // blocks of this segment
     const int64_t b0 = (int64_t)blockIdx.x * kQuantThreads;
     if (b0 >= nb)
         return;                                               // the whole workgroup: past a short last chunk
     const float *src = amax_src + (int64_t)z * amax_stride;
     const float apart = alpha_issue<NPT>(src, n_amax);
-    const int64_t seg0 = unit_row0(k, z, h) * bpr;            // first block of the segment
+    const int64_t seg0 = row0 * bpr;                          // first block of the segment
     const int64_t bl = b0 + threadIdx.x;
     const int64_t b = seg0 + (bl < nb ? bl : nb - 1);         // past the end: re-read the last block
     constexpr int kVec = (int)sizeof(T);
@@ -1090,7 +1096,7 @@ hipError_t launch_kv_quantize_chunked(const void *x, int dtype, int64_t tensors,
     if (nch == 0 || tensors == 0)
         return hipSuccess;
     const int64_t units = tensors * nch;
-    KvChunks k{tokens, tpc, d, heads, (int)nch, kv_chunk_pseg(heads, units)};
+    KvChunks k{tokens, tpc, d, heads, (int)nch, kv_chunk_pseg(heads, units), kv_nch_magic(nch)};
     const float *src = chunk_amax;
     int64_t stride = 1;
     int n_amax = 1;
@@ -1135,7 +1141,8 @@ hipError_t launch_kv_dequantize_chunked(const uint8_t *codes, const uint8_t *sca
     const int64_t nblocks = tensors * heads * tokens * (d / 16);
     if (nblocks == 0)
         return hipSuccess;
-    KvChunks k{tokens, tpc, d, heads, (int)((tokens + tpc - 1) / tpc), 1};
+    const int64_t nch = (tokens + tpc - 1) / tpc;
+    KvChunks k{tokens, tpc, d, heads, (int)nch, 1, kv_nch_magic(nch)};
     const unsigned grid = (unsigned)((nblocks + kQuantThreads - 1) / kQuantThreads);
     if (ydtype == 1)
         k_dequant_kv_chunked<uint16_t><<<grid, kQuantThreads, 0, s>>>(codes, scales, alphas, k, nblocks, (uint16_t *)y);
