@@ -10,6 +10,12 @@ namespace nvfp4 {
 
 constexpr int kQuantThreads = 256;      // threads per quantize workgroup
 constexpr int kRowBlocks = 1;           // 16-element blocks per lane in the ROW16 kernel
+// Inputs of at least this many bytes are read with non-temporal loads by the
+// amax and ROW16 quantize passes; smaller ones with ordinary loads, so that
+// the quantize pass finds part of what the amax pass read in the last-level
+// cache (256 MB).  Thresholds of 64, 128 and 256 MiB measured on 16, 76,
+// 113.5 and 201 MB inputs: 128 MiB was best or level on each.
+constexpr int64_t kStreamLoadBytes = (int64_t)128 << 20;
 constexpr int kAmaxThreads = 1024;      // threads per amax workgroup
 constexpr int kAmaxUnroll = 8;          // 16-byte loads in flight per thread of the per-chunk amax pass
 constexpr int kMaxAmaxPartials = 256;   // amax pass: at most this many workgroups

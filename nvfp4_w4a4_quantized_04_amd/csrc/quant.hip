@@ -78,7 +78,8 @@ __device__ __forceinline__ float absmax16B(uint4 v, float a)
 // TH * U consecutive 16-byte vectors, every thread keeping U loads in flight
 // (the last group's loads are predicated, not serialized); vec: the tensor is
 // contiguous and 16-byte aligned, else rows are read element by element.
-template <typename T, int TH, int U>
+// NT: non-temporal vector loads (large inputs).
+template <typename T, int TH, int U, bool NT>
 __global__ __launch_bounds__(TH) void k_amax(const T *__restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                                              bool vec, float *__restrict__ partials)
 {
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(TH) void k_amax(const T *__restrict__ x, int64_t ro
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int64_t i = g + u * TH + threadIdx.x;
-                v[u] = i < nv ? load_stream(xv + i) : make_uint4(0, 0, 0, 0);
+                v[u] = i < nv ? (NT ? load_stream(xv + i) : xv[i]) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < U; u++)
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_alpha_only(const float *__res
 // registers (blocks b, b+256, ... of the workgroup's range, so every load and
 // store instruction of a wave is contiguous).  Blocks are numbered row-major:
 // block b's codes are bytes [8b, 8b+8), its scale is byte b (cols % 16 == 0).
-template <typename T, bool RULE4, int NPT = 1>
+template <typename T, bool RULE4, int NPT, bool NT>
 __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restrict__ x, int64_t rows, int64_t bpr,
                                                                int64_t ldx, const float *__restrict__ amax_src,
                                                                int n_amax, uint8_t *__restrict__ codes,
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_row16(const T *__restri
         const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
 #pragma unroll
         for (int u = 0; u < kVec; u++)
-            raw[j][u] = load_stream(src + u);
+            raw[j][u] = NT ? load_stream(src + u) : src[u];
     }
     const float alpha = alpha_finish(apart, amax_src, n_amax);
     build_kappa_table(ktab, alpha);
@@ -931,12 +932,16 @@ hipError_t launch_amax(const void *x, int dtype, int64_t rows, int64_t cols, int
     // the flat vector path needs whole 16-byte vectors: entry points that take
     // element-aligned inputs (COL16, WGRAD) fall back to the row loop
     const bool vec = ldx == cols && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+    const bool nt = rows * cols * (dtype == 1 ? 2 : 4) >= kStreamLoadBytes;
+    auto go = [&](auto kernel, auto xt) {
+        kernel<<<n_partials, kAmaxThreads, 0, s>>>(xt, rows, cols, ldx, vec, partials);
+    };
     if (dtype == 1)
-        k_amax<uint16_t, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>((const uint16_t *)x, rows, cols, ldx,
-                                                                             vec, partials);
+        nt ? go(k_amax<uint16_t, kAmaxThreads, 4, true>, (const uint16_t *)x)
+           : go(k_amax<uint16_t, kAmaxThreads, 4, false>, (const uint16_t *)x);
     else
-        k_amax<float, kAmaxThreads, 4><<<n_partials, kAmaxThreads, 0, s>>>((const float *)x, rows, cols, ldx, vec,
-                                                                          partials);
+        nt ? go(k_amax<float, kAmaxThreads, 4, true>, (const float *)x)
+           : go(k_amax<float, kAmaxThreads, 4, false>, (const float *)x);
     return hipGetLastError();
 }
 
@@ -949,12 +954,15 @@ static void launch_quant_t(const T *x, int64_t rows, int64_t cols, int64_t ldx, 
         const int64_t nb = rows * bpr;
         const int64_t per_wg = (int64_t)kQuantThreads * kRowBlocks;
         const unsigned grid = (unsigned)((nb + per_wg - 1) / per_wg);
+        const bool nt = rows * cols * (int64_t)sizeof(T) >= kStreamLoadBytes;
+        auto go = [&](auto kernel) {
+            kernel<<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
+        };
+        constexpr int kNpt4 = kMaxAmaxSrc / kQuantThreads;
         if (n_amax > kQuantThreads)             // up to kMaxAmaxSrc partials (four per thread)
-            k_quant_row16<T, R4, kMaxAmaxSrc / kQuantThreads><<<grid, kQuantThreads, 0, s>>>(
-                x, rows, bpr, ldx, amax_src, n_amax, codes, scales, alpha);
+            nt ? go(k_quant_row16<T, R4, kNpt4, true>) : go(k_quant_row16<T, R4, kNpt4, false>);
         else
-            k_quant_row16<T, R4><<<grid, kQuantThreads, 0, s>>>(x, rows, bpr, ldx, amax_src, n_amax, codes, scales,
-                                                                alpha);
+            nt ? go(k_quant_row16<T, R4, 1, true>) : go(k_quant_row16<T, R4, 1, false>);
     } else if (block == 1) {
         const int64_t tpr = cols / 16;
         const int64_t ty = rows / 16 < 65535 ? rows / 16 : 65535;
