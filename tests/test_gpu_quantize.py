@@ -103,6 +103,18 @@ def test_col16_rht_fp32_and_explicit_amax():
     assert_packed_equal(got2, ref2, "col16 rht fp32 amax")
 
 
+@pytest.mark.parametrize("handed_amax", [False, True])
+def test_row16_fp32_large_input_streaming_loads(handed_amax):
+    # 128 MiB of fp32: at the size from which the amax and ROW16 passes read
+    # with non-temporal loads (ordinary loads below it)
+    rows, cols = 8192, 4096
+    print(f"[case] row16 fp32 [{rows},{cols}] handed_amax={handed_amax}", flush=True)
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-3, 3, (1, cols)))).astype(np.float32)
+    amax = float(np.abs(x).max()) * 1.25 if handed_amax else None
+    _case(x, oracle.ROW16, 1, amax=amax)
+
+
 def test_fp32_input_and_explicit_amax():
     rng = np.random.default_rng(5)
     x = (rng.standard_normal((64, 256)) * 3).astype(np.float32)
