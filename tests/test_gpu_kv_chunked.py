@@ -126,3 +126,31 @@ def test_kv_cache_full_per_chunk():
     call."""
     c = workloads.config4()
     _check(np.stack((c["k"], c["v"])), 8 * 880, 1)
+
+
+def test_units_at_the_limit():
+    """65535 (tensor, chunk) units, the most one call takes: three tensors of
+    21845 one-token chunks.  Each workgroup finds its unit's tensor and chunk
+    with a multiply and shift instead of a division."""
+    kv = workloads.random_bf16(77, (3, 1, 21845, 16), 1.0, 0.01)
+    got = _check(kv, 1, 1)
+    assert got.alphas.shape == (3, 21845)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fuzz_shapes(seed):
+    """Seeded random shapes: tensors, heads, tokens, head_dim, chunk length,
+    rule, input dtype and handed-in chunk maxima."""
+    rng = np.random.default_rng(1000 + seed)
+    tensors = int(rng.integers(1, 4))
+    heads = int(rng.integers(1, 6))
+    tokens = int(rng.integers(1, 301))
+    d = int(rng.choice([16, 32, 48, 64, 128]))
+    tpc = int(rng.integers(1, tokens + 6))
+    rule = int(rng.integers(0, 2))
+    shape = (tensors, heads, tokens, d)
+    if rng.integers(0, 2):
+        kv = workloads.random_bf16(2000 + seed, shape, float(np.exp(rng.uniform(-4, 4))), 0.01)
+    else:
+        kv = (rng.standard_normal(shape) * np.exp(rng.uniform(-4, 4, (1, 1, 1, d)))).astype(np.float32)
+    _check(kv, tpc, rule, chunk_amax=bool(rng.integers(0, 2)))
