@@ -85,10 +85,12 @@ template <int ROWS, bool KFULL, int NSLOT, bool W64 = false>
 struct Producer {
     static constexpr int kTotal = 2 * ROWS;
     static constexpr int kPer = (kTotal + 255) / 256;
+    static_assert(kTotal % 64 == 0, "repeated chunks fill whole producer waves");
     uint32_t code_off[kPer];    // byte offset of the chunk in the code array at step 0
     uint32_t scale_off[kPer];
     uint32_t lds_off[kPer];
     int ch_off[kPer];           // 0 or 16: the chunk's byte offset inside a step
+    bool live[kPer];            // false: the slot only repeats the last chunk
     uint4 codes[NSLOT][kPer];
     uint32_t scales[NSLOT][kPer];
     int rb;                     // code bytes per row (K/2)
@@ -100,7 +102,8 @@ struct Producer {
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
             int q = ptid + 256 * i;
-            q = q < kTotal ? q : kTotal - 1;        // extra threads repeat the last chunk (same data, same place)
+            live[i] = q < kTotal;
+            q = q < kTotal ? q : kTotal - 1;        // extra threads load the last chunk again (never stored)
             const int row = q >> 1, ch = q & 1;
             int gr = row0 + row;
             gr = gr < nrows ? gr : nrows - 1;       // rows past the end re-read the last row; never stored
@@ -144,12 +147,19 @@ struct Producer {
         }
     }
 
-    // decode the chunks of register slot SLOT and write them as fp16 to LDS
+    // decode the chunks of register slot SLOT and write them as fp16 to LDS.
+    // A repeated chunk is neither decoded nor written: LDS writes are the
+    // costly half of the tile traffic (16-byte writes move about 76 B per
+    // clock per CU, reads about 185), and for 192-row operands the repeats
+    // are an eighth of them.  Repeats fill whole waves (kTotal is a multiple
+    // of 64), so the skip is a uniform branch; the loads stay unconditional.
     template <int SLOT>
     __device__ __forceinline__ void store(uint8_t *lds) const
     {
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
+            if (kTotal % 256 != 0 && i == kPer - 1 && !live[i])
+                continue;
             const half2v s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales[SLOT][i], 1.0f, false);
             const half2v lo = {s2[0], s2[0]};
             const half2v hi = {s2[1], s2[1]};
